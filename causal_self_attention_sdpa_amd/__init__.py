@@ -1,0 +1,28 @@
+"""Causal multi-head scaled dot-product self-attention for MI355X (gfx950).
+
+Thin Python binding over the C ABI of `libgattn.so` (declared in
+include/gattn.h).  Every step of the computation runs in the library's HIP
+kernels; this module only checks tensors and passes device pointers, sizes and
+torch's current HIP stream.  There is no fallback: if the library is missing
+or fails to load, importing the binding raises.
+
+Low-level names mirror the C ABI (`gattn_fwd`, `gattn_bwd`, ...) and take
+preallocated torch tensors.  `attention_forward` / `attention_backward`
+allocate the outputs with torch and call those.
+"""
+from ._binding import (  # noqa: F401
+    BF16,
+    F32,
+    GattnError,
+    attention_backward,
+    attention_forward,
+    gattn_bwd,
+    gattn_bwd_finalize,
+    gattn_bwd_main,
+    gattn_bwd_preprocess,
+    gattn_bwd_workspace_bytes,
+    gattn_fwd,
+    gattn_status_string,
+    library_path,
+    load_library,
+)

@@ -1,0 +1,188 @@
+"""ctypes marshalling for libgattn.so.  No computation happens here."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG, "libgattn.so")
+
+F32 = 0
+BF16 = 1
+_STATUS = {0: "GATTN_OK", 1: "GATTN_ERR_INVALID_ARG", 2: "GATTN_ERR_UNSUPPORTED",
+           3: "GATTN_ERR_WORKSPACE", 4: "GATTN_ERR_HIP"}
+
+_lib = None
+
+
+class GattnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what} failed: {_STATUS.get(status, status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Loads libgattn.so (building it first only if it has never been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gattn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.gattn_fwd.restype = i
+    lib.gattn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.gattn_bwd_workspace_bytes.restype = sz
+    lib.gattn_bwd.argtypes = [vp] * 9 + [i, i, i, i, f, i, vp, sz, vp]
+    lib.gattn_bwd.restype = i
+    lib.gattn_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.gattn_bwd_preprocess.restype = i
+    lib.gattn_bwd_main.argtypes = [vp] * 8 + [i, i, i, i, f, i, vp, sz, vp]
+    lib.gattn_bwd_main.restype = i
+    lib.gattn_bwd_finalize.argtypes = [vp, i, i, i, i, i, vp, sz, vp]
+    lib.gattn_bwd_finalize.restype = i
+    lib.gattn_status_string.argtypes = [i]
+    lib.gattn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def gattn_status_string(status: int) -> str:
+    return load_library().gattn_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise GattnError(status, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name: str, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shape4(q):
+    if q.dim() != 4:
+        raise ValueError("expected (B, H, T, hs) tensors")
+    return tuple(int(x) for x in q.shape)
+
+
+def gattn_bwd_workspace_bytes(B: int, H: int, T: int, hs: int, dtype: int) -> int:
+    return int(load_library().gattn_bwd_workspace_bytes(B, H, T, hs, dtype))
+
+
+def gattn_fwd(q, k, v, o, lse, scale: float, stream=None) -> None:
+    """o, lse (lse may be None) <- causal attention of q, k, v on the stream."""
+    lib = load_library()
+    B, H, T, hs = _shape4(q)
+    dt = _dtype_code(q)
+    args = [_dev(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
+    lp = None if lse is None else _dev(lse, "lse", (B, H, T), _torch().float32)
+    _check(lib.gattn_fwd(*args, lp, B, H, T, hs, float(scale), dt, _stream(stream)), "gattn_fwd")
+
+
+def gattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale: float, workspace, stream=None) -> None:
+    lib = load_library()
+    B, H, T, hs = _shape4(q)
+    dt = _dtype_code(q)
+    ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in
+            ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"))]
+    lp = _dev(lse, "lse", (B, H, T), _torch().float32)
+    outs = [_dev(x, n, q.shape, q.dtype) for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.gattn_bwd(*ptrs, lp, *outs, B, H, T, hs, float(scale), dt, ws, nbytes,
+                         _stream(stream)), "gattn_bwd")
+
+
+def gattn_bwd_preprocess(o, dO, workspace, stream=None) -> None:
+    lib = load_library()
+    B, H, T, hs = _shape4(o)
+    ws = _dev(workspace, "workspace")
+    _check(lib.gattn_bwd_preprocess(_dev(o, "o"), _dev(dO, "dO", o.shape, o.dtype), B, H, T, hs,
+                                    _dtype_code(o), ws, workspace.numel() * workspace.element_size(),
+                                    _stream(stream)), "gattn_bwd_preprocess")
+
+
+def gattn_bwd_main(q, k, v, dO, lse, dq, dk, dv, scale: float, workspace, stream=None) -> None:
+    lib = load_library()
+    B, H, T, hs = _shape4(q)
+    dt = _dtype_code(q)
+    ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO"))]
+    lp = _dev(lse, "lse", (B, H, T), _torch().float32)
+    dqp = _dev(dq, "dq", q.shape, q.dtype) if dq is not None else None
+    outs = [_dev(x, n, q.shape, q.dtype) for x, n in ((dk, "dk"), (dv, "dv"))]
+    _check(lib.gattn_bwd_main(*ptrs, lp, dqp, *outs, B, H, T, hs, float(scale), dt,
+                              _dev(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gattn_bwd_main")
+
+
+def gattn_bwd_finalize(dq, workspace, stream=None) -> None:
+    lib = load_library()
+    B, H, T, hs = _shape4(dq)
+    _check(lib.gattn_bwd_finalize(_dev(dq, "dq"), B, H, T, hs, _dtype_code(dq),
+                                  _dev(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gattn_bwd_finalize")
+
+
+def _default_scale(hs: int, scale):
+    return 1.0 / math.sqrt(hs) if scale is None else float(scale)
+
+
+def attention_forward(q, k, v, scale=None, need_lse: bool = True, stream=None):
+    """Returns (o, lse) for (B, H, T, hs) device tensors; lse is None if not needed."""
+    torch = _torch()
+    B, H, T, hs = _shape4(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if need_lse else None
+    gattn_fwd(q, k, v, o, lse, _default_scale(hs, scale), stream)
+    return o, lse
+
+
+def attention_backward(q, k, v, o, dO, lse, scale=None, workspace=None, stream=None):
+    """Returns (dq, dk, dv); allocates the workspace unless one is given."""
+    torch = _torch()
+    B, H, T, hs = _shape4(q)
+    if workspace is None:
+        n = gattn_bwd_workspace_bytes(B, H, T, hs, _dtype_code(q))
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    gattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, _default_scale(hs, scale), workspace, stream)
+    return dq, dk, dv

@@ -1,0 +1,145 @@
+// C-ABI entry points of libgattn: argument validation (before any HIP call)
+// and dispatch to the float32 or bf16 kernels.  Semantics and error codes are
+// documented in include/gattn.h.
+#include "gattn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "gattn_internal.h"
+
+namespace {
+
+using gattn::ws_d_bytes;
+using gattn::ws_dq_bytes;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool ptr_ok(const void* p) { return p != nullptr && aligned(p, 16); }
+
+int check_shape(int B, int H, int T, int hs, int dtype) {
+  if (B < 1 || H < 1 || T < 1 || hs < 1) return GATTN_ERR_INVALID_ARG;
+  if (dtype != GATTN_F32 && dtype != GATTN_BF16) return GATTN_ERR_INVALID_ARG;
+  if (int64_t(B) * H * T * hs >= (int64_t(1) << 31)) return GATTN_ERR_INVALID_ARG;
+  if (dtype == GATTN_BF16 && hs != 32 && hs != 64) return GATTN_ERR_UNSUPPORTED;
+  if (dtype == GATTN_F32 && hs > 128) return GATTN_ERR_UNSUPPORTED;
+  return GATTN_OK;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+int check_workspace(const void* ws, size_t bytes, int B, int H, int T, int hs, int dtype) {
+  if (ws == nullptr || !aligned(ws, 256)) return GATTN_ERR_WORKSPACE;
+  if (bytes < gattn_bwd_workspace_bytes(B, H, T, hs, dtype)) return GATTN_ERR_WORKSPACE;
+  return GATTN_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? GATTN_OK : GATTN_ERR_HIP; }
+
+float* ws_D(void* ws, int B, int H, int T, int hs, int dtype) {
+  return reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                  ws_dq_bytes(B, H, T, hs, dtype == GATTN_BF16));
+}
+float* ws_dq(void* ws) { return static_cast<float*>(ws); }
+
+}  // namespace
+
+extern "C" {
+
+const char* gattn_status_string(int status) {
+  switch (status) {
+    case GATTN_OK: return "GATTN_OK";
+    case GATTN_ERR_INVALID_ARG: return "GATTN_ERR_INVALID_ARG";
+    case GATTN_ERR_UNSUPPORTED: return "GATTN_ERR_UNSUPPORTED";
+    case GATTN_ERR_WORKSPACE: return "GATTN_ERR_WORKSPACE";
+    case GATTN_ERR_HIP: return "GATTN_ERR_HIP";
+    default: return "GATTN_UNKNOWN_STATUS";
+  }
+}
+
+size_t gattn_bwd_workspace_bytes(int B, int H, int T, int hs, int dtype) {
+  if (check_shape(B, H, T, hs, dtype) != GATTN_OK) return 0;
+  return ws_dq_bytes(B, H, T, hs, dtype == GATTN_BF16) + ws_d_bytes(B, H, T);
+}
+
+int gattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+              int T, int hs, float scale, int dtype, hipStream_t stream) {
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o)) return GATTN_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 16)) return GATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return GATTN_ERR_INVALID_ARG;
+  if (int st = check_shape(B, H, T, hs, dtype)) return st;
+  const int BH = B * H;
+  if (dtype == GATTN_F32)
+    return status_of(gattn::f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
+                                    static_cast<const float*>(v), static_cast<float*>(o), lse, BH,
+                                    T, hs, scale, stream));
+  return status_of(gattn::bf16_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                   static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+                                   BH, T, hs, scale, stream));
+}
+
+int gattn_bwd_preprocess(const void* o, const void* dO, int B, int H, int T, int hs, int dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr_ok(o) || !ptr_ok(dO)) return GATTN_ERR_INVALID_ARG;
+  if (int st = check_shape(B, H, T, hs, dtype)) return st;
+  if (int st = check_workspace(workspace, workspace_bytes, B, H, T, hs, dtype)) return st;
+  float* D = ws_D(workspace, B, H, T, hs, dtype);
+  if (dtype == GATTN_F32)
+    return status_of(gattn::f32_bwd_pre(static_cast<const float*>(o), static_cast<const float*>(dO),
+                                        D, B * H, T, hs, stream));
+  return status_of(gattn::bf16_bwd_pre(static_cast<const uint16_t*>(o),
+                                       static_cast<const uint16_t*>(dO), D, ws_dq(workspace),
+                                       B * H, T, hs, stream));
+}
+
+int gattn_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int T, int hs, float scale,
+                   int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(dO) || !ptr_ok(lse) || !ptr_ok(dk) ||
+      !ptr_ok(dv))
+    return GATTN_ERR_INVALID_ARG;
+  if (dtype == GATTN_F32 && !ptr_ok(dq)) return GATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return GATTN_ERR_INVALID_ARG;
+  if (int st = check_shape(B, H, T, hs, dtype)) return st;
+  if (int st = check_workspace(workspace, workspace_bytes, B, H, T, hs, dtype)) return st;
+  const float* D = ws_D(workspace, B, H, T, hs, dtype);
+  if (dtype == GATTN_F32)
+    return status_of(gattn::f32_bwd_main(
+        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+        static_cast<const float*>(dO), lse, D, static_cast<float*>(dq), static_cast<float*>(dk),
+        static_cast<float*>(dv), B * H, T, hs, scale, stream));
+  return status_of(gattn::bf16_bwd_main(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), lse, D, ws_dq(workspace),
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B * H, T, hs, scale, stream));
+}
+
+int gattn_bwd_finalize(void* dq, int B, int H, int T, int hs, int dtype, const void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (!ptr_ok(dq)) return GATTN_ERR_INVALID_ARG;
+  if (int st = check_shape(B, H, T, hs, dtype)) return st;
+  if (int st = check_workspace(workspace, workspace_bytes, B, H, T, hs, dtype)) return st;
+  if (dtype == GATTN_F32) return GATTN_OK;
+  return status_of(gattn::bf16_bwd_fin(static_cast<const float*>(workspace),
+                                       static_cast<uint16_t*>(dq), B * H, T, hs, stream));
+}
+
+int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, void* dq, void* dk, void* dv, int B, int H, int T, int hs,
+              float scale, int dtype, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  // Validate everything up front so that a rejected call enqueues nothing.
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(dO) || !ptr_ok(lse) ||
+      !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv))
+    return GATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return GATTN_ERR_INVALID_ARG;
+  if (int st = check_shape(B, H, T, hs, dtype)) return st;
+  if (int st = check_workspace(workspace, workspace_bytes, B, H, T, hs, dtype)) return st;
+  int st = gattn_bwd_preprocess(o, dO, B, H, T, hs, dtype, workspace, workspace_bytes, stream);
+  if (st != GATTN_OK) return st;
+  st = gattn_bwd_main(q, k, v, dO, lse, dq, dk, dv, B, H, T, hs, scale, dtype, workspace,
+                      workspace_bytes, stream);
+  if (st != GATTN_OK) return st;
+  return gattn_bwd_finalize(dq, B, H, T, hs, dtype, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+/*
+ * gattn — causal multi-head scaled dot-product self-attention for MI355X (gfx950).
+ *
+ * What is computed (per batch b and head h, independently: heads run in
+ * parallel, "Let's build GPT" summary page, timestamp 1:22:27):
+ *
+ *   S[i][j] = scale * sum_d Q[i][d] * K[j][d]     affinity of query i with key j
+ *                                                 (1:04:00-1:06:16); scale is
+ *                                                 normally 1/sqrt(hs) (1:17:18)
+ *   S[i][j] = -inf for j > i                      lower-triangular tril mask, the
+ *                                                 diagonal kept (48:54, 55:20)
+ *   P[i][:] = softmax(S[i][:])                    each row sums to one (51:04)
+ *   O[i][:] = sum_j P[i][j] * V[j][:]             the value is what gets passed on
+ *                                                 (1:10:15)
+ *   lse[i]  = ln sum_{j<=i} exp(S[i][j])          natural log, float32
+ *
+ * The backward (the pages only say the model is trained by backprop) is the
+ * chain rule of the above: with D[i] = sum_d dO[i][d] * O[i][d],
+ * dS[i][j] = P[i][j] * (dO[i].V[j] - D[i]),
+ *   dV[j] = sum_{i>=j} P[i][j] dO[i],  dQ[i] = scale * sum_{j<=i} dS[i][j] K[j],
+ *   dK[j] = scale * sum_{i>=j} dS[i][j] Q[i].
+ *
+ * Layout: every tensor is contiguous (B, H, T, hs), row-major, hs innermost;
+ * lse and D are contiguous (B, H, T) float32.  The T x T mask is never
+ * materialised.
+ *
+ * Dtypes: q, k, v, o, dO, dq, dk, dv all have `dtype`; lse is always float32.
+ *   GATTN_BF16: hs in {32, 64}; MFMA kernels, bf16 inputs/outputs, float32
+ *               accumulation, every float32 -> bf16 conversion rounds to
+ *               nearest even.
+ *   GATTN_F32 : any hs in [1, 128]; float32 throughout (deterministic).
+ *
+ * Ownership: every pointer is a device pointer owned by the caller.  The
+ * library allocates nothing and keeps no state; calls are re-entrant.  Work is
+ * enqueued on `stream` (0 = the null stream) and the call returns without
+ * waiting; buffers must stay alive until that stream has finished it.
+ * Outputs (o, lse, dq, dk, dv, workspace) are overwritten, never accumulated,
+ * and must not alias any input.
+ *
+ * Errors: every function returns a gattn_status.  All argument checks run
+ * before any HIP call, so an invalid call enqueues nothing.  INVALID_ARG: a
+ * required pointer is NULL or not 16-byte aligned, B, H or T < 1, hs < 1,
+ * scale not finite or <= 0, B*H*T*hs >= 2^31, or dtype unknown.
+ * UNSUPPORTED: bf16 with hs not in {32, 64}, or f32 with hs > 128.
+ * WORKSPACE: workspace NULL or smaller than gattn_bwd_workspace_bytes().
+ * HIP: a kernel launch failed (the HIP error is not cleared from the caller's
+ * view beyond what hipLaunchKernel itself reports).
+ */
+#ifndef GATTN_H
+#define GATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GATTN_F32 = 0, GATTN_BF16 = 1 } gattn_dtype;
+
+typedef enum {
+  GATTN_OK = 0,
+  GATTN_ERR_INVALID_ARG = 1,
+  GATTN_ERR_UNSUPPORTED = 2,
+  GATTN_ERR_WORKSPACE = 3,
+  GATTN_ERR_HIP = 4
+} gattn_status;
+
+/*
+ * Forward: o = softmax(mask_causal(scale * q k^T)) v, and lse.
+ * Passages: tril mask and -inf fill (48:54, 55:20), row softmax (51:04),
+ * query.key affinity scaled by 1/sqrt(head size) (1:06:16, 1:17:18), weighted
+ * sum of values (1:10:15), one head per (b, h) (1:22:27).
+ *   q, k, v : inputs, (B, H, T, hs), `dtype`.
+ *   o       : output, (B, H, T, hs), `dtype`.
+ *   lse     : output, (B, H, T) float32, natural log; may be NULL when no
+ *             backward will follow (inference).
+ *   scale   : multiplier of q.k (> 0, finite), normally 1/sqrt(hs).
+ */
+int gattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int H, int T, int hs, float scale, int dtype, hipStream_t stream);
+
+/*
+ * Bytes of device workspace gattn_bwd needs: for bf16 a float32 dQ
+ * accumulator (B*H*T*hs) plus D (B*H*T), each 256-byte aligned; for f32 just D.
+ * Returns 0 for arguments gattn_bwd would reject.
+ */
+size_t gattn_bwd_workspace_bytes(int B, int H, int T, int hs, int dtype);
+
+/*
+ * Backward: dq, dk, dv of L = sum(dO * o) for the forward above (chain rule;
+ * the pages state only that training runs a backward pass).
+ *   q, k, v, o, dO : inputs (B, H, T, hs), `dtype`; o is what gattn_fwd wrote.
+ *   lse            : input (B, H, T) float32, what gattn_fwd wrote (required).
+ *   dq, dk, dv     : outputs (B, H, T, hs), `dtype`.
+ *   workspace      : caller-owned device memory of at least
+ *                    gattn_bwd_workspace_bytes() bytes, 256-byte aligned; the
+ *                    library overwrites it (it needs no clearing).
+ * Equivalent to gattn_bwd_preprocess, gattn_bwd_main, gattn_bwd_finalize in
+ * that order on `stream`.  For bf16, dq is accumulated with float32 atomics, so
+ * dq may differ in the last bits from run to run; dk, dv and every f32 output
+ * are deterministic.
+ */
+int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, void* dq, void* dk, void* dv,
+              int B, int H, int T, int hs, float scale, int dtype,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward stage 1: D[i] = sum_d dO[i][d] * o[i][d] into the workspace, and
+ * (bf16) the float32 dQ accumulator in the workspace set to zero.
+ */
+int gattn_bwd_preprocess(const void* o, const void* dO, int B, int H, int T, int hs, int dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward stage 2: recomputes P from q, k and lse, writes dk and dv, and
+ * accumulates dq: bf16 into the workspace accumulator (dq is not touched);
+ * f32 directly into dq.  Needs stage 1's workspace contents.
+ */
+int gattn_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int T, int hs, float scale,
+                   int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward stage 3 (bf16): dq = bf16(accumulator), round to nearest even.
+ * For f32 it enqueues nothing and returns GATTN_OK.
+ */
+int gattn_bwd_finalize(void* dq, int B, int H, int T, int hs, int dtype, const void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Static, human-readable name of a gattn_status value. */
+const char* gattn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GATTN_H */

@@ -1,0 +1,81 @@
+"""Shared helpers for the GPU tests: run the library through the C ABI and the
+oracle on the same seeded inputs, and compare."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+import synth_inputs as si
+
+OUT_NAMES = ("dq", "dk", "dv", "o", "lse")
+
+
+def torch_dtype(dtype: str):
+    import torch
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+
+
+def to_dev(a: np.ndarray, dtype: str):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch_dtype(dtype))
+
+
+def gpu_fwd_bwd(x: dict, dtype: str, scale: float, use_stages: bool = False):
+    """Runs gattn_fwd then gattn_bwd; returns float64 numpy (dq, dk, dv, o, lse)."""
+    import torch
+    import causal_self_attention_sdpa_amd as ga
+    t = {n: to_dev(a, dtype) for n, a in x.items()}
+    B, H, T, hs = x["q"].shape
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    ga.gattn_fwd(t["q"], t["k"], t["v"], o, lse, scale)
+    ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16 if dtype == "bf16" else ga.F32),
+                     dtype=torch.uint8, device="cuda")
+    dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
+    if use_stages:
+        ga.gattn_bwd_preprocess(o, t["do"], ws)
+        ga.gattn_bwd_main(t["q"], t["k"], t["v"], t["do"], lse, dq, dk, dv, scale, ws)
+        ga.gattn_bwd_finalize(dq, ws)
+    else:
+        ga.gattn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, dq, dk, dv, scale, ws)
+    torch.cuda.synchronize()
+    return tuple(a.float().cpu().numpy().astype(np.float64) for a in (dq, dk, dv, o, lse))
+
+
+def max_abs(a, b) -> float:
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def check_close(got, ref, tol: float, rel: float = 0.0, names=OUT_NAMES, where: str = ""):
+    """Elementwise |got - ref| <= tol + rel*|ref| for every output."""
+    report = {}
+    for n, g, r in zip(names, got, ref):
+        err = np.abs(g - r)
+        bound = tol + rel * np.abs(r)
+        report[n] = max_abs(g, r)
+        bad = np.argwhere(~(err <= bound))
+        assert bad.size == 0, (f"{where} {n}: {len(bad)} elements out of tolerance; first at "
+                               f"{tuple(bad[0])}: got {g[tuple(bad[0])]}, ref {r[tuple(bad[0])]}, "
+                               f"max abs err {report[n]}")
+    return report
+
+
+def inputs(B, H, T, hs, dtype, seed=1234, workload="test", layer=0, qkv_scale=1.0):
+    return si.attention_inputs(B, H, T, hs, dtype, seed=seed, workload=workload, layer=layer,
+                               qkv_scale=qkv_scale)
+
+
+def oracle_slices(x: dict, scale: float, slices):
+    """Oracle on selected (b, h) slices: returns outputs shaped (n, 1, T, hs)."""
+    sel = {n: np.stack([a[b, h] for b, h in slices])[:, None] for n, a in x.items()}
+    return oracle.attention_backward(sel["q"], sel["k"], sel["v"], sel["do"], scale)
+
+
+def pick(got, slices):
+    return tuple(np.stack([a[b, h] for b, h in slices])[:, None] for a in got)
+
+
+def default_scale(hs: int) -> float:
+    return 1.0 / math.sqrt(hs)

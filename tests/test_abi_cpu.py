@@ -1,0 +1,110 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gattn.h declares, and rejects bad arguments before any HIP call (so
+no compute is enqueued; the fake pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import causal_self_attention_sdpa_amd as ga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "gattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gattn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ga.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert "gattn_fwd" in names and "gattn_bwd" in names
+    raw = ctypes.CDLL(ga.library_path())
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings(lib):
+    assert ga.gattn_status_string(OK) == "GATTN_OK"
+    assert ga.gattn_status_string(INVALID) == "GATTN_ERR_INVALID_ARG"
+    assert ga.gattn_status_string(UNSUPPORTED) == "GATTN_ERR_UNSUPPORTED"
+    assert ga.gattn_status_string(WORKSPACE) == "GATTN_ERR_WORKSPACE"
+    assert ga.gattn_status_string(HIP) == "GATTN_ERR_HIP"
+    assert ga.gattn_status_string(99) == "GATTN_UNKNOWN_STATUS"
+
+
+def test_workspace_bytes(lib):
+    B, H, T, hs = 12, 12, 1024, 64
+    n = ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16)
+    assert n == B * H * T * hs * 4 + B * H * T * 4
+    assert ga.gattn_bwd_workspace_bytes(4, 4, 8, 8, ga.F32) == 512  # 4*4*8 floats, 256-aligned
+    assert ga.gattn_bwd_workspace_bytes(1, 1, 3, 64, ga.BF16) == 768 + 256
+    assert ga.gattn_bwd_workspace_bytes(1, 1, 3, 32, ga.BF16) == 512 + 256
+    assert ga.gattn_bwd_workspace_bytes(0, 1, 1, 64, ga.BF16) == 0
+    assert ga.gattn_bwd_workspace_bytes(1, 1, 1, 48, ga.BF16) == 0  # unsupported hs
+    assert ga.gattn_bwd_workspace_bytes(1, 1, 1, 8, 7) == 0
+
+
+P = 0x10000  # fake, 256-aligned "device" address, never touched
+
+
+def _fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, T=8, hs=64, scale=0.125, dtype=1):
+    return lib.gattn_fwd(q, k, v, o, lse, B, H, T, hs, scale, dtype, None)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(lib, q=None) == INVALID
+    assert _fwd(lib, o=None) == INVALID
+    assert _fwd(lib, k=P + 2) == INVALID      # misaligned
+    assert _fwd(lib, lse=P + 4) == INVALID    # misaligned lse
+    for bad in (dict(B=0), dict(H=-1), dict(T=0), dict(hs=0)):
+        assert _fwd(lib, **bad) == INVALID, bad
+    for s in (0.0, -1.0, float("inf"), float("nan")):
+        assert _fwd(lib, scale=s) == INVALID, s
+    assert _fwd(lib, dtype=5) == INVALID
+    assert _fwd(lib, B=1 << 11, H=1 << 10, T=1 << 10, hs=64) == INVALID  # >= 2^31 elements
+    assert _fwd(lib, hs=48) == UNSUPPORTED
+    assert _fwd(lib, hs=128) == UNSUPPORTED
+    assert _fwd(lib, hs=129, dtype=0) == UNSUPPORTED
+
+
+def _bwd(lib, ptrs=None, B=1, H=1, T=8, hs=64, scale=0.125, dtype=1, ws=P, wsb=1 << 20):
+    p = ptrs or [P] * 9
+    return lib.gattn_bwd(*p, B, H, T, hs, scale, dtype, ws, wsb, None)
+
+
+def test_bwd_validation(lib):
+    for i in range(9):
+        p = [P] * 9
+        p[i] = None
+        assert _bwd(lib, p) == INVALID, i
+        p[i] = P + 8
+        assert _bwd(lib, p) == INVALID, i
+    assert _bwd(lib, scale=float("nan")) == INVALID
+    assert _bwd(lib, hs=16) == UNSUPPORTED
+    assert _bwd(lib, ws=None) == WORKSPACE
+    assert _bwd(lib, ws=P + 16) == WORKSPACE  # not 256-aligned
+    need = ga.gattn_bwd_workspace_bytes(1, 1, 8, 64, 1)
+    assert _bwd(lib, wsb=need - 1) == WORKSPACE
+
+
+def test_stage_validation(lib):
+    assert lib.gattn_bwd_preprocess(None, P, 1, 1, 8, 64, 1, P, 1 << 20, None) == INVALID
+    assert lib.gattn_bwd_preprocess(P, P, 1, 1, 8, 64, 1, P, 1, None) == WORKSPACE
+    assert lib.gattn_bwd_main(P, P, P, P, P, None, P, P, 1, 1, 8, 64, 0.0, 1, P, 1 << 20,
+                              None) == INVALID
+    # f32 main needs dq; bf16 main does not (dq comes from finalize)
+    assert lib.gattn_bwd_main(P, P, P, P, P, None, P, P, 1, 1, 8, 8, 0.5, 0, P, 1 << 20,
+                              None) == INVALID
+    assert lib.gattn_bwd_finalize(None, 1, 1, 8, 64, 1, P, 1 << 20, None) == INVALID
+    assert lib.gattn_bwd_finalize(P, 1, 1, 8, 64, 1, P, 2, None) == WORKSPACE
+    # f32 finalize is a no-op that enqueues nothing
+    assert lib.gattn_bwd_finalize(P, 1, 1, 8, 8, 0, P, 1 << 20, None) == OK

@@ -1,0 +1,122 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element
+by element, on the same seeded inputs.
+
+Bars (max-abs over every element of o, lse, dq, dk, dv):
+  * f32 path: 1e-4;
+  * bf16 path with unit-variance inputs (and the x0.5 variant): 2e-2;
+  * bf16 with inputs x2.0 (softmax-range stress): |err| <= 2e-2 + 2^-8 |ref|
+    (bf16 output rounding alone reaches 2^-8 |ref| there).
+Small shapes are checked in full; full-size shapes on sampled (b, h) slices,
+each slice computed independently by the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from gpu_util import check_close, default_scale, gpu_fwd_bwd, inputs, oracle_slices, pick
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+BF16_TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import causal_self_attention_sdpa_amd as ga
+    ga.load_library()
+
+
+def _full(B, H, T, hs, dtype, tol, rel=0.0, qkv_scale=1.0, seed=1234, stages=False):
+    x = inputs(B, H, T, hs, dtype, seed=seed, qkv_scale=qkv_scale)
+    s = default_scale(hs)
+    print(f"case {dtype} B={B} H={H} T={T} hs={hs} x{qkv_scale} seed={seed}", flush=True)
+    got = gpu_fwd_bwd(x, dtype, s, use_stages=stages)
+    import oracle
+    ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], s)
+    return check_close(got, ref, tol, rel, where=f"{dtype} {(B, H, T, hs)}")
+
+
+# ---------------------------------------------------------------- f32 path
+def test_f32_tiny_config():
+    """Tiny character-level shape: B=4, H=4, T=8, hs=8, fp32, scale 1/sqrt(8)."""
+    _full(4, 4, 8, 8, "f32", F32_TOL)
+
+
+@pytest.mark.parametrize("B,H,T,hs", [(1, 1, 1, 8), (2, 3, 67, 16), (1, 2, 130, 100),
+                                      (1, 1, 200, 128), (3, 1, 5, 1), (1, 2, 64, 65)])
+def test_f32_shapes(B, H, T, hs):
+    _full(B, H, T, hs, "f32", F32_TOL)
+
+
+def test_f32_stages_equal_composite():
+    _full(2, 2, 33, 8, "f32", F32_TOL, stages=True)
+
+
+def test_f32_deterministic():
+    x = inputs(2, 2, 50, 24, "f32", seed=5)
+    a = gpu_fwd_bwd(x, "f32", 0.2)
+    b = gpu_fwd_bwd(x, "f32", 0.2)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+# ---------------------------------------------------------------- bf16 path
+@pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 257, 300])
+@pytest.mark.parametrize("hs", [64, 32])
+def test_bf16_ragged_lengths(T, hs):
+    """Tile-boundary and ragged-tail lengths, every element checked."""
+    _full(2, 3, T, hs, "bf16", BF16_TOL, seed=100 + T)
+
+
+def test_bf16_several_tiles_full_check():
+    _full(2, 2, 640, 64, "bf16", BF16_TOL, seed=9)
+
+
+def test_bf16_stages_equal_composite():
+    _full(1, 3, 190, 64, "bf16", BF16_TOL, stages=True)
+
+
+def test_bf16_char_level_reduced_batch():
+    """Char-level GPT shape (H=6, T=256, hs=64) with B=2, every element."""
+    _full(2, 6, 256, 64, "bf16", BF16_TOL)
+
+
+def test_bf16_narrow_heads_full():
+    """Narrow-head shape B=8, H=12, hs=32 at T=128 and T=256, every element."""
+    _full(8, 12, 128, 32, "bf16", BF16_TOL, seed=31)
+    _full(8, 12, 256, 32, "bf16", BF16_TOL, seed=32)
+
+
+def _sampled(B, H, T, hs, qkv_scale, slices, tol, rel, seed, layer=0):
+    x = inputs(B, H, T, hs, "bf16", seed=seed, layer=layer, qkv_scale=qkv_scale,
+               workload=f"b{B}h{H}t{T}d{hs}")
+    s = default_scale(hs)
+    print(f"case bf16 full-size B={B} H={H} T={T} hs={hs} x{qkv_scale} slices={slices}", flush=True)
+    got = gpu_fwd_bwd(x, "bf16", s)
+    ref = oracle_slices(x, s, slices)
+    return check_close(pick(got, slices), ref, tol, rel, where=f"bf16 {(B, H, T, hs)} x{qkv_scale}")
+
+
+def test_bf16_char_level_full_size():
+    """B=64, H=6, T=256, hs=64: full launch, sampled slices."""
+    _sampled(64, 6, 256, 64, 1.0, [(0, 0), (17, 3), (63, 5)], BF16_TOL, 0.0, 1)
+
+
+def test_bf16_gpt2_small_half_scale():
+    """B=12, H=12, T=1024, hs=64, q/k/v x0.5: full launch, sampled slices."""
+    _sampled(12, 12, 1024, 64, 0.5, [(0, 0), (5, 7), (11, 11)], BF16_TOL, 0.0, 2)
+
+
+def test_bf16_gpt2_small_double_scale():
+    """Same shape, q/k/v x2.0: stress of the softmax range."""
+    _sampled(12, 12, 1024, 64, 2.0, [(0, 0), (6, 4), (11, 11)], BF16_TOL, 2.0 ** -8, 2)
+
+
+def test_bf16_gpt2_xl_heads():
+    """B=12, H=25 (odd head count), T=1024, hs=64: full launch, sampled slices."""
+    _sampled(12, 25, 1024, 64, 1.0, [(0, 0), (3, 24), (11, 12)], BF16_TOL, 0.0, 3)
