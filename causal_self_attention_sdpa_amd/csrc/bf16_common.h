@@ -33,6 +33,35 @@ __device__ inline f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c)
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Row permutation for the A operand of a 32x32 MFMA: swapping bits 2 and 3
+// of the row index makes result register i of lane l hold row
+// 16*(i/8) + 8*(l/32) + i%8, so each lane's registers 8t..8t+7 cover 8
+// consecutive rows: the k-slot layout of a following MFMA's operand.
+__device__ inline int perm_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ds_read_b64_tr_b16 (gfx950 LDS transpose read).  Within each group of 16
+// lanes, every lane names an 8-byte segment (4 bf16); output element e of
+// lane i of the group is element i%4 of the segment named by lane 4e + i/4.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ inline u32x2 ds_read_tr(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// 32x32x16 MFMA operand (lane l holds n = l%32 and k = 8*(l/32) .. +7, i.e.
+// the B layout, which is also the A layout with m in place of n) read from a
+// row-major LDS matrix M[k][n] with row stride `st` elements, for the block
+// k0 .. k0+15, n0 .. n0+31.  Two transpose reads, rows +0..3 and +4..7.
+__device__ inline u32x4 lds_operand_tr(const uint16_t* M, int st, int k0, int n0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const uint16_t* p = M + (k0 + 8 * (g >> 1) + (j >> 2)) * st + n0 + 16 * (g & 1) + 4 * (j & 3);
+  const u32x2 a = ds_read_tr(p), b = ds_read_tr(p + 4 * st);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 // Reductions across the two 32-lane halves of a wavefront (lanes l and l^32)
 // with v_permlane32_swap: swap(x, x) yields the pair (x[l], x[l^32]) in every lane.
 __device__ inline float halves_max(float x) {

@@ -31,8 +31,6 @@
 namespace gattn {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 template <int HS>
 struct FwdCfg {
   static constexpr int NW = 4;              // wavefronts per workgroup
@@ -46,8 +44,6 @@ struct FwdCfg {
   static constexpr int VU = (BN / 8) * (HS / 2);        // V transpose units (8 keys x 2 d)
   static_assert(KPT >= 1 && VU % 64 == 0 && VU <= 64 * NW, "tile shape");
 };
-
-__device__ inline int perm_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
 template <int HS>
 __global__ __launch_bounds__(256) void bf16_fwd_kernel(const uint16_t* __restrict__ q,

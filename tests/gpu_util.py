@@ -77,5 +77,57 @@ def pick(got, slices):
     return tuple(np.stack([a[b, h] for b, h in slices])[:, None] for a in got)
 
 
+U_BF16 = 2.0 ** -8  # unit roundoff of bfloat16 (8 significant bits)
+
+
+def rounding_bound(x: dict, scale: float, slices, ref):
+    """First-order bound on the error of the bf16 path, per element, for the
+    selected (b, h) slices, derived from where that path rounds:
+      o  = P V           P rounded to bf16 before the MFMA
+      dv = P^T dO        P rounded
+      dk = s dS^T Q      dS rounded; D = rowsum(dO * O) uses the bf16-stored O
+      dq = s dS K        same
+    plus the rounding of the stored bf16 output itself (u |ref|).  Terms are
+    float64 magnitudes built from the inputs and the oracle's lse:
+    |err| <= u (|ref| + Mag) with Mag = sum of |operand products|."""
+    u = U_BF16
+    sel = {n: np.stack([a[b, h] for b, h in slices]) for n, a in x.items()}
+    dq_r, dk_r, dv_r, o_r, lse_r = (a[:, 0] for a in ref)
+    T = sel["q"].shape[1]
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    s = np.einsum("nid,njd->nij", sel["q"], sel["k"]) * scale
+    P = np.where(causal, np.exp(np.where(causal, s, 0.0) - lse_r[:, :, None]), 0.0)
+    A = np.sum(np.abs(sel["do"]) * np.abs(o_r), axis=-1)          # |dO|.|O| per row
+    D = np.sum(sel["do"] * o_r, axis=-1)
+    dP = np.einsum("nid,njd->nij", sel["do"], sel["v"])
+    dS = P * (dP - D[:, :, None])
+    W = np.abs(dS) + P * A[:, :, None]
+    mag = {
+        "o": P @ np.abs(sel["v"]),
+        "dv": np.swapaxes(P, 1, 2) @ np.abs(sel["do"]),
+        "dk": scale * np.swapaxes(W, 1, 2) @ np.abs(sel["q"]),
+        "dq": scale * W @ np.abs(sel["k"]),
+    }
+    out = []
+    for n, r in zip(OUT_NAMES, (dq_r, dk_r, dv_r, o_r, lse_r)):
+        if n == "lse":
+            out.append(np.full(r.shape, 1e-3)[:, None])
+        else:
+            out.append((u * (np.abs(r) + mag[n]) + 1e-3)[:, None])
+    return tuple(out)
+
+
+def check_bound(got, ref, bound, names=OUT_NAMES, where: str = ""):
+    """Elementwise |got - ref| <= bound; returns the largest err/bound ratio."""
+    worst = {}
+    for n, g, r, b in zip(names, got, ref, bound):
+        ratio = np.abs(g - r) / b
+        worst[n] = float(ratio.max())
+        bad = np.argwhere(~(ratio <= 1.0))
+        assert bad.size == 0, (f"{where} {n}: {len(bad)} elements above the rounding bound; "
+                               f"worst ratio {worst[n]:.3f}")
+    return worst
+
+
 def default_scale(hs: int) -> float:
     return 1.0 / math.sqrt(hs)
