@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of the causal attention hot path (forward + backward) on one GPU.
+
+One step = the forward of every layer (0 .. L-1) followed by the backward of
+every layer (L-1 .. 0), each layer with its own resident input buffers, on
+the GPT-2 124M attention shape: B=12, H=12, T=1024, hs=64, bf16, 12 layers,
+q/k/v ~ N(0,1) x 0.5 and dO ~ N(0,1) (seeded, synthetic).
+
+FLOP accounting (the pages' attention term of the MFU estimate, 12 H hs T per
+token per layer with the backward at twice the forward, restricted to the
+causal pairs j <= i, P_c = T (T + 1) / 2 per (b, h)):
+    forward 4 hs P_c B H, backward 8 hs P_c B H.
+
+Prints one JSON line.  `roofline` is for the dominant kernel (the backward
+main kernel): algorithmic FLOP per launch / its mean duration measured with
+HIP events recorded on the launch stream inside the timed steps.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0
+METRIC = "causal attention fwd+bwd TFLOP/s at B12 H12 T1024 hs64; % of bf16 MFMA peak"
+WORKLOAD = dict(B=12, H=12, T=1024, hs=64, layers=12, qkv_scale=0.5)
+DOMINANT = "bf16_bwd_kernel<64>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_b12h12t1024_traffic.txt")
+BWD_SOURCE = os.path.join(ROOT, "causal_self_attention_sdpa_amd", "csrc", "bf16_bwd.hip")
+
+
+def flops(B, H, T, hs):
+    pc = T * (T + 1) // 2
+    return 4 * hs * pc * B * H, 8 * hs * pc * B * H
+
+
+def source_digest(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(launch_flops: float):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None when that summary is absent or was taken on a
+    different version of the kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_digest(BWD_SOURCE):
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(x, scale, nslices: int):
+    """The CPU oracle (as it stands) on the first `nslices` (b, h) slices of
+    layer 0, all host threads of this process's CPU share (at most 16)."""
+    import numpy as np
+
+    import oracle
+
+    B, H, T, hs = x["q"].shape
+    idx = [(b, h) for b in range(B) for h in range(H)][:nslices]
+    sel = {n: np.stack([a[b, h] for b, h in idx])[:, None] for n, a in x.items()}
+    threads = min(16, len(os.sched_getaffinity(0)))
+    t0 = time.perf_counter()
+    oracle.attention_backward(sel["q"], sel["k"], sel["v"], sel["do"], scale, nthreads=threads)
+    dt = time.perf_counter() - t0
+    ff, fb = flops(len(idx), 1, T, hs)
+    return {"value": round((ff + fb) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{len(idx)} of {B * H} (b,h) slices of layer 0 (T={T}, hs={hs}), "
+                      f"forward+backward in float64, FLOP counted as on the GPU"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-slices", type=int, default=48,
+                    help="(b,h) slices the CPU oracle baseline runs (0 to skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention core shards over (b, h) with no exchange; see the design notes).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import causal_self_attention_sdpa_amd as ga
+    import synth_inputs as si
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = 1 << 28  # 256 MiB of float32 read and written once
+        a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}))
+        return 0
+
+    W = WORKLOAD
+    B, H, T, hs, L = W["B"], W["H"], W["T"], W["hs"], W["layers"]
+    scale = 1.0 / math.sqrt(hs)
+    print(f"[bench] generating {L} layers of seeded inputs {B}x{H}x{T}x{hs}", file=sys.stderr,
+          flush=True)
+    layers = []
+    host0 = None
+    for l in range(L):
+        x = si.attention_inputs(B, H, T, hs, "bf16", seed=2024, workload="gpt2-124m-attn", layer=l,
+                                qkv_scale=W["qkv_scale"])
+        if l == 0:
+            host0 = x
+        t = {n: torch.from_numpy(a).to(dev).to(torch.bfloat16) for n, a in x.items()}
+        t["o"] = torch.empty_like(t["q"])
+        t["lse"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        for g in ("dq", "dk", "dv"):
+            t[g] = torch.empty_like(t["q"])
+        layers.append(t)
+    ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+    nb = args.steps * L
+    ev_b = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(nb)]
+    ev_f = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(nb)]
+
+    def step(record: int | None):
+        for l in range(L):
+            t = layers[l]
+            if record is not None:
+                ev_f[record * L + l][0].record(stream)
+            ga.gattn_fwd(t["q"], t["k"], t["v"], t["o"], t["lse"], scale)
+            if record is not None:
+                ev_f[record * L + l][1].record(stream)
+        for l in reversed(range(L)):
+            t = layers[l]
+            ga.gattn_bwd_preprocess(t["o"], t["do"], ws)
+            if record is not None:
+                ev_b[record * L + l][0].record(stream)
+            ga.gattn_bwd_main(t["q"], t["k"], t["v"], t["do"], t["lse"], None, t["dk"], t["dv"],
+                              scale, ws)
+            if record is not None:
+                ev_b[record * L + l][1].record(stream)
+            ga.gattn_bwd_finalize(t["dq"], ws)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(s)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    ff, fb = flops(B, H, T, hs)
+    step_flops = L * (ff + fb)
+    ms_per_step = dt / args.steps * 1e3
+    value = step_flops * args.steps / dt / 1e12
+    bwd_us = float(np.mean([a.elapsed_time(b) for a, b in ev_b])) * 1e3
+    fwd_us = float(np.mean([a.elapsed_time(b) for a, b in ev_f])) * 1e3
+    achieved = fb / (bwd_us * 1e-6) / 1e12
+    traffic = read_traffic(fb)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "pct_of_bf16_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 3),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GPT-2 124M causal attention, fwd+bwd, 12 layers",
+                   "B": B, "H": H, "T": T, "hs": hs, "layers": L, "qkv_scale": W["qkv_scale"],
+                   "flop_count": "causal pairs, fwd 4*hs, bwd 8*hs per pair",
+                   "parallelism": "single GPU"},
+        "kernels_us": {"fwd": round(fwd_us, 2), "bwd_main": round(bwd_us, 2)},
+        "roofline": {"kernel": DOMINANT, "bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    if args.cpu_slices > 0:
+        print(f"[bench] timing the CPU oracle on {args.cpu_slices} slices", file=sys.stderr,
+              flush=True)
+        out["cpu_baseline"] = cpu_baseline(host0, scale, args.cpu_slices)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
