@@ -11,9 +11,12 @@ token per layer with the backward at twice the forward, restricted to the
 causal pairs j <= i, P_c = T (T + 1) / 2 per (b, h)):
     forward 4 hs P_c B H, backward 8 hs P_c B H.
 
-Prints one JSON line.  `roofline` is for the dominant kernel (the backward
-main kernel): algorithmic FLOP per launch / its mean duration measured with
-HIP events recorded on the launch stream inside the timed steps.
+Prints one JSON line.  `roofline` is for the dominant kernel (the one with the
+largest mean duration): its algorithmic FLOP per launch / that mean duration,
+measured with HIP events recorded on the launch stream inside the timed steps.
+Algorithmic FLOP per causal pair and kernel: forward 4 hs (Q K^T and P V);
+dK/dV kernel 6 hs (dO V^T, P^T dO, dS^T Q; its Q K^T is recomputation); dQ
+kernel 2 hs (dS K; its Q K^T and dO V^T are recomputation).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -35,9 +38,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal attention fwd+bwd TFLOP/s at B12 H12 T1024 hs64; % of bf16 MFMA peak"
 WORKLOAD = dict(B=12, H=12, T=1024, hs=64, layers=12, qkv_scale=0.5)
-DOMINANT = "bf16_bwd_kernel<64>"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_b12h12t1024_traffic.txt")
-BWD_SOURCE = os.path.join(ROOT, "causal_self_attention_sdpa_amd", "csrc", "bf16_bwd.hip")
+CSRC = os.path.join(ROOT, "causal_self_attention_sdpa_amd", "csrc")
+KERNELS = {  # name -> (kernel symbol, source file, algorithmic FLOP per causal pair / hs)
+    "fwd": ("bf16_fwd_kernel<64>", "bf16_fwd.hip", 4),
+    "dkdv": ("bf16_dkdv_kernel<64>", "bf16_bwd.hip", 6),
+    "dq": ("bf16_dq_kernel<64>", "bf16_bwd.hip", 2),
+}
 
 
 def flops(B, H, T, hs):
@@ -49,16 +55,18 @@ def source_digest(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(launch_flops: float):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, or None when that summary is absent or was taken on a
-    different version of the kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(name: str):
+    """HBM bytes per launch of kernel `name` from the committed rocprofv3
+    counter summary (profiles/<name>_b12h12t1024_traffic.txt), or None when
+    that summary is absent or was taken on a different version of the kernel
+    source."""
+    path = os.path.join(ROOT, "profiles", f"{name}_b12h12t1024_traffic.txt")
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != source_digest(BWD_SOURCE):
+    if not m or not t or m.group(1) != source_digest(os.path.join(CSRC, KERNELS[name][1])):
         return None
     return float(t.group(1))
 
@@ -140,29 +148,47 @@ def main() -> int:
                      device=dev)
     stream = torch.cuda.current_stream()
     nb = args.steps * L
-    ev_b = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(nb)]
-    ev_f = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(nb)]
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(nb)] for k in KERNELS}
+
+    # C-ABI argument tuples, marshalled once: the timed loop is nothing but
+    # library calls (and event records), so the host keeps ahead of the GPU.
+    lib = ga.load_library()
+    sp = stream.cuda_stream
+    p = lambda x: x.data_ptr()
+    wsb = ws.numel()
+    call = []
+    for t in layers:
+        call.append({
+            "fwd": (lib.gattn_fwd, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["lse"]),
+                                    B, H, T, hs, scale, ga.BF16, sp)),
+            "pre": (lib.gattn_bwd_preprocess, (p(t["o"]), p(t["do"]), B, H, T, hs, ga.BF16,
+                                               p(ws), wsb, sp)),
+            "dkdv": (lib.gattn_bwd_dkdv, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["do"]),
+                                          p(t["lse"]), p(t["dk"]), p(t["dv"]), B, H, T, hs, scale,
+                                          ga.BF16, p(ws), wsb, sp)),
+            "dq": (lib.gattn_bwd_dq, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["do"]), p(t["lse"]),
+                                      p(t["dq"]), B, H, T, hs, scale, ga.BF16, p(ws), wsb, sp)),
+        })
+
+    def run(l, name, idx):
+        fn, a = call[l][name]
+        if idx is not None and name in ev:
+            ev[name][idx][0].record(stream)
+        st = fn(*a)
+        if idx is not None and name in ev:
+            ev[name][idx][1].record(stream)
+        if st != 0:
+            raise RuntimeError(f"{name} failed with status {st}")
 
     def step(record: int | None):
         for l in range(L):
-            t = layers[l]
-            if record is not None:
-                ev_f[record * L + l][0].record(stream)
-            ga.gattn_fwd(t["q"], t["k"], t["v"], t["o"], t["lse"], scale)
-            if record is not None:
-                ev_f[record * L + l][1].record(stream)
+            run(l, "fwd", None if record is None else record * L + l)
         for l in reversed(range(L)):
-            t = layers[l]
-            ga.gattn_bwd_preprocess(t["o"], t["do"], ws)
-            if record is not None:
-                ev_b[record * L + l][0].record(stream)
-            ga.gattn_bwd_main(t["q"], t["k"], t["v"], t["do"], t["lse"], None, t["dk"], t["dv"],
-                              scale, ws)
-            if record is not None:
-                ev_b[record * L + l][1].record(stream)
-            ga.gattn_bwd_finalize(t["dq"], ws)
+            i = None if record is None else record * L + l
+            run(l, "pre", i)
+            run(l, "dkdv", i)
+            run(l, "dq", i)
 
     for _ in range(args.warmup):
         step(None)
@@ -178,10 +204,11 @@ def main() -> int:
     step_flops = L * (ff + fb)
     ms_per_step = dt / args.steps * 1e3
     value = step_flops * args.steps / dt / 1e12
-    bwd_us = float(np.mean([a.elapsed_time(b) for a, b in ev_b])) * 1e3
-    fwd_us = float(np.mean([a.elapsed_time(b) for a, b in ev_f])) * 1e3
-    achieved = fb / (bwd_us * 1e-6) / 1e12
-    traffic = read_traffic(fb)
+    pairs = B * H * T * (T + 1) // 2
+    mean_us = {k: float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) * 1e3 for k in KERNELS}
+    dom = max(mean_us, key=mean_us.get)
+    alg = KERNELS[dom][2] * hs * pairs
+    achieved = alg / (mean_us[dom] * 1e-6) / 1e12
 
     out = {
         "metric": METRIC,
@@ -201,11 +228,12 @@ def main() -> int:
                    "B": B, "H": H, "T": T, "hs": hs, "layers": L, "qkv_scale": W["qkv_scale"],
                    "flop_count": "causal pairs, fwd 4*hs, bwd 8*hs per pair",
                    "parallelism": "single GPU"},
-        "kernels_us": {"fwd": round(fwd_us, 2), "bwd_main": round(bwd_us, 2)},
-        "roofline": {"kernel": DOMINANT, "bound": "mfma", "achieved": round(achieved, 3),
+        "kernels_us": {k: round(v, 2) for k, v in mean_us.items()},
+        "roofline": {"kernel": KERNELS[dom][0], "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic},
+                     "traffic": read_traffic(dom),
+                     "algorithmic_flop_per_launch": alg},
     }
     if args.cpu_slices > 0:
         print(f"[bench] timing the CPU oracle on {args.cpu_slices} slices", file=sys.stderr,

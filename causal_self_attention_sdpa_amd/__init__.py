@@ -17,8 +17,8 @@ from ._binding import (  # noqa: F401
     attention_backward,
     attention_forward,
     gattn_bwd,
-    gattn_bwd_finalize,
-    gattn_bwd_main,
+    gattn_bwd_dkdv,
+    gattn_bwd_dq,
     gattn_bwd_preprocess,
     gattn_bwd_workspace_bytes,
     gattn_fwd,

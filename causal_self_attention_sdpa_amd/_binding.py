@@ -44,10 +44,10 @@ def load_library():
     lib.gattn_bwd.restype = i
     lib.gattn_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
     lib.gattn_bwd_preprocess.restype = i
-    lib.gattn_bwd_main.argtypes = [vp] * 8 + [i, i, i, i, f, i, vp, sz, vp]
-    lib.gattn_bwd_main.restype = i
-    lib.gattn_bwd_finalize.argtypes = [vp, i, i, i, i, i, vp, sz, vp]
-    lib.gattn_bwd_finalize.restype = i
+    lib.gattn_bwd_dkdv.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp, sz, vp]
+    lib.gattn_bwd_dkdv.restype = i
+    lib.gattn_bwd_dq.argtypes = [vp] * 6 + [i, i, i, i, f, i, vp, sz, vp]
+    lib.gattn_bwd_dq.restype = i
     lib.gattn_status_string.argtypes = [i]
     lib.gattn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -139,27 +139,27 @@ def gattn_bwd_preprocess(o, dO, workspace, stream=None) -> None:
                                     _stream(stream)), "gattn_bwd_preprocess")
 
 
-def gattn_bwd_main(q, k, v, dO, lse, dq, dk, dv, scale: float, workspace, stream=None) -> None:
+def gattn_bwd_dkdv(q, k, v, dO, lse, dk, dv, scale: float, workspace, stream=None) -> None:
     lib = load_library()
     B, H, T, hs = _shape4(q)
-    dt = _dtype_code(q)
     ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO"))]
     lp = _dev(lse, "lse", (B, H, T), _torch().float32)
-    dqp = _dev(dq, "dq", q.shape, q.dtype) if dq is not None else None
     outs = [_dev(x, n, q.shape, q.dtype) for x, n in ((dk, "dk"), (dv, "dv"))]
-    _check(lib.gattn_bwd_main(*ptrs, lp, dqp, *outs, B, H, T, hs, float(scale), dt,
+    _check(lib.gattn_bwd_dkdv(*ptrs, lp, *outs, B, H, T, hs, float(scale), _dtype_code(q),
                               _dev(workspace, "workspace"),
                               workspace.numel() * workspace.element_size(), _stream(stream)),
-           "gattn_bwd_main")
+           "gattn_bwd_dkdv")
 
 
-def gattn_bwd_finalize(dq, workspace, stream=None) -> None:
+def gattn_bwd_dq(q, k, v, dO, lse, dq, scale: float, workspace, stream=None) -> None:
     lib = load_library()
-    B, H, T, hs = _shape4(dq)
-    _check(lib.gattn_bwd_finalize(_dev(dq, "dq"), B, H, T, hs, _dtype_code(dq),
-                                  _dev(workspace, "workspace"),
-                                  workspace.numel() * workspace.element_size(), _stream(stream)),
-           "gattn_bwd_finalize")
+    B, H, T, hs = _shape4(q)
+    ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO"))]
+    lp = _dev(lse, "lse", (B, H, T), _torch().float32)
+    _check(lib.gattn_bwd_dq(*ptrs, lp, _dev(dq, "dq", q.shape, q.dtype), B, H, T, hs,
+                            float(scale), _dtype_code(q), _dev(workspace, "workspace"),
+                            workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gattn_bwd_dq")
 
 
 def _default_scale(hs: int, scale):

@@ -62,6 +62,27 @@ __device__ inline u32x4 lds_operand_tr(const uint16_t* M, int st, int k0, int n0
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// Buffer resources: raw (stride 0) buffers whose size bounds every access in
+// hardware.  Loads past `bytes` return zero and stores past it are dropped,
+// so row tails need no branches.  The fourth descriptor word is the gfx9
+// raw-buffer format (32-bit data format, no swizzle).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+__device__ inline u32x4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline float bloadf(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, off, 0, 0);
+}
+__device__ inline void bstoref(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+
 // Reductions across the two 32-lane halves of a wavefront (lanes l and l^32)
 // with v_permlane32_swap: swap(x, x) yields the pair (x[l], x[l^32]) in every lane.
 __device__ inline float halves_max(float x) {

@@ -216,20 +216,22 @@ hipError_t f32_bwd_pre(const float* o, const float* dO, float* D, int BH, int T,
   return launch(f32_pre_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, o, dO, D, BH, T, hs);
 }
 
-hipError_t f32_bwd_main(const float* q, const float* k, const float* v, const float* dO,
-                        const float* lse, const float* D, float* dq, float* dk, float* dv, int BH,
-                        int T, int hs, float scale, hipStream_t s) {
-  hipError_t e;
-  if (hs <= 64) {
-    e = launch(f32_dkdv_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D, dk,
-               dv, BH, T, hs, scale);
-    if (e != hipSuccess) return e;
+hipError_t f32_bwd_dkdv(const float* q, const float* k, const float* v, const float* dO,
+                        const float* lse, const float* D, float* dk, float* dv, int BH, int T,
+                        int hs, float scale, hipStream_t s) {
+  if (hs <= 64)
+    return launch(f32_dkdv_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D,
+                  dk, dv, BH, T, hs, scale);
+  return launch(f32_dkdv_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D, dk,
+                dv, BH, T, hs, scale);
+}
+
+hipError_t f32_bwd_dq(const float* q, const float* k, const float* v, const float* dO,
+                      const float* lse, const float* D, float* dq, int BH, int T, int hs,
+                      float scale, hipStream_t s) {
+  if (hs <= 64)
     return launch(f32_dq_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D,
                   dq, BH, T, hs, scale);
-  }
-  e = launch(f32_dkdv_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D, dk,
-             dv, BH, T, hs, scale);
-  if (e != hipSuccess) return e;
   return launch(f32_dq_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D, dq,
                 BH, T, hs, scale);
 }

@@ -26,11 +26,8 @@ hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t str
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, 0, stream);
 }
 
-// Workspace layout for the backward: [dQ accumulator f32 (bf16 only)][D f32].
+// Backward workspace: D = rowsum(dO * O), float32 (B, H, T), 256-byte aligned size.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-inline size_t ws_dq_bytes(int B, int H, int T, int hs, bool bf16) {
-  return bf16 ? align256(sizeof(float) * size_t(B) * H * T * hs) : 0;
-}
 inline size_t ws_d_bytes(int B, int H, int T) { return align256(sizeof(float) * size_t(B) * H * T); }
 
 // ---- float32 path (any hs <= 128, any T; wave per row; deterministic) ----
@@ -38,19 +35,23 @@ hipError_t f32_fwd(const float* q, const float* k, const float* v, float* o, flo
                    int T, int hs, float scale, hipStream_t s);
 hipError_t f32_bwd_pre(const float* o, const float* dO, float* D, int BH, int T, int hs,
                        hipStream_t s);
-hipError_t f32_bwd_main(const float* q, const float* k, const float* v, const float* dO,
-                        const float* lse, const float* D, float* dq, float* dk, float* dv, int BH,
-                        int T, int hs, float scale, hipStream_t s);
+hipError_t f32_bwd_dkdv(const float* q, const float* k, const float* v, const float* dO,
+                        const float* lse, const float* D, float* dk, float* dv, int BH, int T,
+                        int hs, float scale, hipStream_t s);
+hipError_t f32_bwd_dq(const float* q, const float* k, const float* v, const float* dO,
+                      const float* lse, const float* D, float* dq, int BH, int T, int hs,
+                      float scale, hipStream_t s);
 
 // ---- bf16 path (hs in {32, 64}; MFMA) ----
 hipError_t bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                     float* lse, int BH, int T, int hs, float scale, hipStream_t s);
-hipError_t bf16_bwd_pre(const uint16_t* o, const uint16_t* dO, float* D, float* dq_acc, int BH,
-                        int T, int hs, hipStream_t s);
-hipError_t bf16_bwd_main(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const uint16_t* dO, const float* lse, const float* D, float* dq_acc,
-                         uint16_t* dk, uint16_t* dv, int BH, int T, int hs, float scale,
-                         hipStream_t s);
-hipError_t bf16_bwd_fin(const float* dq_acc, uint16_t* dq, int BH, int T, int hs, hipStream_t s);
+hipError_t bf16_bwd_pre(const uint16_t* o, const uint16_t* dO, float* D, int BH, int T, int hs,
+                        hipStream_t s);
+hipError_t bf16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dO, const float* lse, const float* D, uint16_t* dk,
+                         uint16_t* dv, int BH, int T, int hs, float scale, hipStream_t s);
+hipError_t bf16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                       const uint16_t* dO, const float* lse, const float* D, uint16_t* dq, int BH,
+                       int T, int hs, float scale, hipStream_t s);
 
 }  // namespace gattn

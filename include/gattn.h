@@ -42,7 +42,8 @@
  * required pointer is NULL or not 16-byte aligned, B, H or T < 1, hs < 1,
  * scale not finite or <= 0, B*H*T*hs >= 2^31, or dtype unknown.
  * UNSUPPORTED: bf16 with hs not in {32, 64}, or f32 with hs > 128.
- * WORKSPACE: workspace NULL or smaller than gattn_bwd_workspace_bytes().
+ * WORKSPACE: workspace NULL, not 256-byte aligned, or smaller than
+ * gattn_bwd_workspace_bytes().
  * HIP: a kernel launch failed (the HIP error is not cleared from the caller's
  * view beyond what hipLaunchKernel itself reports).
  */
@@ -81,9 +82,9 @@ int gattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int T, int hs, float scale, int dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace gattn_bwd needs: for bf16 a float32 dQ
- * accumulator (B*H*T*hs) plus D (B*H*T), each 256-byte aligned; for f32 just D.
- * Returns 0 for arguments gattn_bwd would reject.
+ * Bytes of device workspace gattn_bwd needs: D = rowsum(dO * o), float32
+ * (B, H, T), rounded up to a multiple of 256.  Returns 0 for arguments
+ * gattn_bwd would reject.
  */
 size_t gattn_bwd_workspace_bytes(int B, int H, int T, int hs, int dtype);
 
@@ -96,10 +97,8 @@ size_t gattn_bwd_workspace_bytes(int B, int H, int T, int hs, int dtype);
  *   workspace      : caller-owned device memory of at least
  *                    gattn_bwd_workspace_bytes() bytes, 256-byte aligned; the
  *                    library overwrites it (it needs no clearing).
- * Equivalent to gattn_bwd_preprocess, gattn_bwd_main, gattn_bwd_finalize in
- * that order on `stream`.  For bf16, dq is accumulated with float32 atomics, so
- * dq may differ in the last bits from run to run; dk, dv and every f32 output
- * are deterministic.
+ * Equivalent to gattn_bwd_preprocess, gattn_bwd_dkdv, gattn_bwd_dq in that
+ * order on `stream`.  Every output is deterministic (no atomics).
  */
 int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
               const float* lse, void* dq, void* dk, void* dv,
@@ -107,27 +106,28 @@ int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Backward stage 1: D[i] = sum_d dO[i][d] * o[i][d] into the workspace, and
- * (bf16) the float32 dQ accumulator in the workspace set to zero.
+ * Backward stage 1: D[i] = sum_d dO[i][d] * o[i][d] (float32) into the
+ * workspace; D is the row term of dS = P (dP - D).
  */
 int gattn_bwd_preprocess(const void* o, const void* dO, int B, int H, int T, int hs, int dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Backward stage 2: recomputes P from q, k and lse, writes dk and dv, and
- * accumulates dq: bf16 into the workspace accumulator (dq is not touched);
- * f32 directly into dq.  Needs stage 1's workspace contents.
+ * Backward stage 2: dk and dv.  Recomputes P from q, k and lse (exactly 0
+ * above the diagonal) and dS from dO, v and stage 1's D.
+ *   dk = scale * dS^T q,  dv = P^T dO.
  */
-int gattn_bwd_main(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                   void* dq, void* dk, void* dv, int B, int H, int T, int hs, float scale,
-                   int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                   void* dk, void* dv, int B, int H, int T, int hs, float scale, int dtype,
+                   const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Backward stage 3 (bf16): dq = bf16(accumulator), round to nearest even.
- * For f32 it enqueues nothing and returns GATTN_OK.
+ * Backward stage 3: dq = scale * dS k, recomputing P and dS as stage 2 does.
+ * Independent of stage 2's outputs (both need only stage 1's D).
  */
-int gattn_bwd_finalize(void* dq, int B, int H, int T, int hs, int dtype, const void* workspace,
-                       size_t workspace_bytes, hipStream_t stream);
+int gattn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                 void* dq, int B, int H, int T, int hs, float scale, int dtype,
+                 const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a gattn_status value. */
 const char* gattn_status_string(int status);

@@ -36,8 +36,8 @@ def gpu_fwd_bwd(x: dict, dtype: str, scale: float, use_stages: bool = False):
     dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
     if use_stages:
         ga.gattn_bwd_preprocess(o, t["do"], ws)
-        ga.gattn_bwd_main(t["q"], t["k"], t["v"], t["do"], lse, dq, dk, dv, scale, ws)
-        ga.gattn_bwd_finalize(dq, ws)
+        ga.gattn_bwd_dq(t["q"], t["k"], t["v"], t["do"], lse, dq, scale, ws)
+        ga.gattn_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], lse, dk, dv, scale, ws)
     else:
         ga.gattn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, dq, dk, dv, scale, ws)
     torch.cuda.synchronize()

@@ -44,10 +44,10 @@ def test_status_strings(lib):
 def test_workspace_bytes(lib):
     B, H, T, hs = 12, 12, 1024, 64
     n = ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16)
-    assert n == B * H * T * hs * 4 + B * H * T * 4
+    assert n == B * H * T * 4  # D only
     assert ga.gattn_bwd_workspace_bytes(4, 4, 8, 8, ga.F32) == 512  # 4*4*8 floats, 256-aligned
-    assert ga.gattn_bwd_workspace_bytes(1, 1, 3, 64, ga.BF16) == 768 + 256
-    assert ga.gattn_bwd_workspace_bytes(1, 1, 3, 32, ga.BF16) == 512 + 256
+    assert ga.gattn_bwd_workspace_bytes(1, 1, 3, 64, ga.BF16) == 256
+    assert ga.gattn_bwd_workspace_bytes(1, 1, 65, 32, ga.BF16) == 512
     assert ga.gattn_bwd_workspace_bytes(0, 1, 1, 64, ga.BF16) == 0
     assert ga.gattn_bwd_workspace_bytes(1, 1, 1, 48, ga.BF16) == 0  # unsupported hs
     assert ga.gattn_bwd_workspace_bytes(1, 1, 1, 8, 7) == 0
@@ -99,12 +99,18 @@ def test_bwd_validation(lib):
 def test_stage_validation(lib):
     assert lib.gattn_bwd_preprocess(None, P, 1, 1, 8, 64, 1, P, 1 << 20, None) == INVALID
     assert lib.gattn_bwd_preprocess(P, P, 1, 1, 8, 64, 1, P, 1, None) == WORKSPACE
-    assert lib.gattn_bwd_main(P, P, P, P, P, None, P, P, 1, 1, 8, 64, 0.0, 1, P, 1 << 20,
-                              None) == INVALID
-    # f32 main needs dq; bf16 main does not (dq comes from finalize)
-    assert lib.gattn_bwd_main(P, P, P, P, P, None, P, P, 1, 1, 8, 8, 0.5, 0, P, 1 << 20,
-                              None) == INVALID
-    assert lib.gattn_bwd_finalize(None, 1, 1, 8, 64, 1, P, 1 << 20, None) == INVALID
-    assert lib.gattn_bwd_finalize(P, 1, 1, 8, 64, 1, P, 2, None) == WORKSPACE
-    # f32 finalize is a no-op that enqueues nothing
-    assert lib.gattn_bwd_finalize(P, 1, 1, 8, 8, 0, P, 1 << 20, None) == OK
+    assert lib.gattn_bwd_preprocess(P, P, 1, 1, 8, 48, 1, P, 1 << 20, None) == UNSUPPORTED
+    # dkdv: q, k, v, dO, lse, dk, dv
+    for i in range(7):
+        p = [P] * 7
+        p[i] = None
+        assert lib.gattn_bwd_dkdv(*p, 1, 1, 8, 64, 0.125, 1, P, 1 << 20, None) == INVALID, i
+    assert lib.gattn_bwd_dkdv(*([P] * 7), 1, 1, 8, 64, 0.0, 1, P, 1 << 20, None) == INVALID
+    assert lib.gattn_bwd_dkdv(*([P] * 7), 1, 1, 8, 64, 0.125, 1, P, 4, None) == WORKSPACE
+    # dq: q, k, v, dO, lse, dq
+    for i in range(6):
+        p = [P] * 6
+        p[i] = P + 4
+        assert lib.gattn_bwd_dq(*p, 1, 1, 8, 64, 0.125, 1, P, 1 << 20, None) == INVALID, i
+    assert lib.gattn_bwd_dq(*([P] * 6), 1, 1, 8, 200, 0.125, 0, P, 1 << 20, None) == UNSUPPORTED
+    assert lib.gattn_bwd_dq(*([P] * 6), 1, 1, 8, 64, 0.125, 1, None, 1 << 20, None) == WORKSPACE
