@@ -41,8 +41,8 @@ WORKLOAD = dict(B=12, H=12, T=1024, hs=64, layers=12, qkv_scale=0.5)
 CSRC = os.path.join(ROOT, "causal_self_attention_sdpa_amd", "csrc")
 KERNELS = {  # name -> (kernel symbol, source file, algorithmic FLOP per causal pair / hs)
     "fwd": ("bf16_fwd_kernel<64>", "bf16_fwd.hip", 4),
-    "dkdv": ("bf16_dkdv_kernel<64>", "bf16_bwd.hip", 6),
     "dq": ("bf16_dq_kernel<64>", "bf16_bwd.hip", 2),
+    "dkdv": ("bf16_dkdv_kernel<64>", "bf16_bwd.hip", 6),
 }
 
 
@@ -162,13 +162,12 @@ def main() -> int:
         call.append({
             "fwd": (lib.gattn_fwd, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["lse"]),
                                     B, H, T, hs, scale, ga.BF16, sp)),
-            "pre": (lib.gattn_bwd_preprocess, (p(t["o"]), p(t["do"]), B, H, T, hs, ga.BF16,
-                                               p(ws), wsb, sp)),
+            "dq": (lib.gattn_bwd_dq, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["do"]),
+                                      p(t["lse"]), p(t["dq"]), B, H, T, hs, scale, ga.BF16, p(ws),
+                                      wsb, sp)),
             "dkdv": (lib.gattn_bwd_dkdv, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["do"]),
-                                          p(t["lse"]), p(t["dk"]), p(t["dv"]), B, H, T, hs, scale,
-                                          ga.BF16, p(ws), wsb, sp)),
-            "dq": (lib.gattn_bwd_dq, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["do"]), p(t["lse"]),
-                                      p(t["dq"]), B, H, T, hs, scale, ga.BF16, p(ws), wsb, sp)),
+                                          p(t["dk"]), p(t["dv"]), B, H, T, hs, scale, ga.BF16,
+                                          p(ws), wsb, sp)),
         })
 
     def run(l, name, idx):
@@ -186,9 +185,8 @@ def main() -> int:
             run(l, "fwd", None if record is None else record * L + l)
         for l in reversed(range(L)):
             i = None if record is None else record * L + l
-            run(l, "pre", i)
-            run(l, "dkdv", i)
             run(l, "dq", i)
+            run(l, "dkdv", i)
 
     for _ in range(args.warmup):
         step(None)

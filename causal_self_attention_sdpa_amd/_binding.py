@@ -42,12 +42,12 @@ def load_library():
     lib.gattn_bwd_workspace_bytes.restype = sz
     lib.gattn_bwd.argtypes = [vp] * 9 + [i, i, i, i, f, i, vp, sz, vp]
     lib.gattn_bwd.restype = i
-    lib.gattn_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.gattn_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
     lib.gattn_bwd_preprocess.restype = i
-    lib.gattn_bwd_dkdv.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp, sz, vp]
-    lib.gattn_bwd_dkdv.restype = i
-    lib.gattn_bwd_dq.argtypes = [vp] * 6 + [i, i, i, i, f, i, vp, sz, vp]
+    lib.gattn_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp, sz, vp]
     lib.gattn_bwd_dq.restype = i
+    lib.gattn_bwd_dkdv.argtypes = [vp] * 6 + [i, i, i, i, f, i, vp, sz, vp]
+    lib.gattn_bwd_dkdv.restype = i
     lib.gattn_status_string.argtypes = [i]
     lib.gattn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -130,36 +130,37 @@ def gattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale: float, workspace, stream=N
                          _stream(stream)), "gattn_bwd")
 
 
-def gattn_bwd_preprocess(o, dO, workspace, stream=None) -> None:
+def gattn_bwd_preprocess(o, dO, lse, workspace, stream=None) -> None:
     lib = load_library()
     B, H, T, hs = _shape4(o)
-    ws = _dev(workspace, "workspace")
-    _check(lib.gattn_bwd_preprocess(_dev(o, "o"), _dev(dO, "dO", o.shape, o.dtype), B, H, T, hs,
-                                    _dtype_code(o), ws, workspace.numel() * workspace.element_size(),
-                                    _stream(stream)), "gattn_bwd_preprocess")
+    _check(lib.gattn_bwd_preprocess(_dev(o, "o"), _dev(dO, "dO", o.shape, o.dtype),
+                                    _dev(lse, "lse", (B, H, T), _torch().float32), B, H, T, hs,
+                                    _dtype_code(o), _dev(workspace, "workspace"),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gattn_bwd_preprocess")
 
 
-def gattn_bwd_dkdv(q, k, v, dO, lse, dk, dv, scale: float, workspace, stream=None) -> None:
+def gattn_bwd_dq(q, k, v, o, dO, lse, dq, scale: float, workspace, stream=None) -> None:
     lib = load_library()
     B, H, T, hs = _shape4(q)
-    ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO"))]
-    lp = _dev(lse, "lse", (B, H, T), _torch().float32)
-    outs = [_dev(x, n, q.shape, q.dtype) for x, n in ((dk, "dk"), (dv, "dv"))]
-    _check(lib.gattn_bwd_dkdv(*ptrs, lp, *outs, B, H, T, hs, float(scale), _dtype_code(q),
-                              _dev(workspace, "workspace"),
-                              workspace.numel() * workspace.element_size(), _stream(stream)),
-           "gattn_bwd_dkdv")
-
-
-def gattn_bwd_dq(q, k, v, dO, lse, dq, scale: float, workspace, stream=None) -> None:
-    lib = load_library()
-    B, H, T, hs = _shape4(q)
-    ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO"))]
+    ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in
+            ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"))]
     lp = _dev(lse, "lse", (B, H, T), _torch().float32)
     _check(lib.gattn_bwd_dq(*ptrs, lp, _dev(dq, "dq", q.shape, q.dtype), B, H, T, hs,
                             float(scale), _dtype_code(q), _dev(workspace, "workspace"),
                             workspace.numel() * workspace.element_size(), _stream(stream)),
            "gattn_bwd_dq")
+
+
+def gattn_bwd_dkdv(q, k, v, dO, dk, dv, scale: float, workspace, stream=None) -> None:
+    lib = load_library()
+    B, H, T, hs = _shape4(q)
+    ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO"))]
+    outs = [_dev(x, n, q.shape, q.dtype) for x, n in ((dk, "dk"), (dv, "dv"))]
+    _check(lib.gattn_bwd_dkdv(*ptrs, *outs, B, H, T, hs, float(scale), _dtype_code(q),
+                              _dev(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream)),
+           "gattn_bwd_dkdv")
 
 
 def _default_scale(hs: int, scale):

@@ -1,4 +1,4 @@
-// bf16 causal attention backward on gfx950 MFMA: three kernels, no atomics.
+// bf16 causal attention backward on gfx950 MFMA: two main kernels, no atomics.
 //
 // The pages state only that the model is trained with a backward pass; the
 // gradients are the chain rule of the forward ("Let's build GPT" summary
@@ -6,23 +6,34 @@
 // 1:17:18, weighted values 1:10:15):
 //   P  = exp(scale * Q K^T - lse)    recomputed from the forward's lse,
 //                                    exactly 0 above the diagonal
-//   D  = rowsum(dO * O)              (preprocess kernel)
+//   D  = rowsum(dO * O)
 //   dP = dO V^T,   dS = P * (dP - D)
+//   dQ = scale * dS K                          (dQ kernel, per query tile; it
+//                                               also writes D and lse*log2(e)
+//                                               to the workspace)
 //   dV = P^T dO,   dK = scale * dS^T Q        (dK/dV kernel, per key tile)
-//   dQ = scale * dS K                          (dQ kernel, per query tile)
 // Splitting dQ from dK/dV costs a second recomputation of S and dP, and in
 // exchange removes float32 atomics (which on this chip are executed past the
 // per-XCD L2s), the zeroing and conversion passes of an accumulator, and the
 // LDS round trip of dS; every output is deterministic.
 //
-// Both main kernels stream tiles through double-buffered LDS with one barrier
-// per step: the loads for step t+1 are in flight (in registers) while step t
-// computes.  Global accesses go through buffer resources sized to one (b, h)
-// slice, so rows past T read as zero and their stores are dropped.
+// Both kernels stream tiles into double-buffered, swizzled LDS tiles by LDS
+// DMA (no register staging) with one barrier per step: the DMA for step t+1
+// runs while step t computes.  Global accesses go through buffer resources
+// sized to one (b, h) slice, so rows past T read as zero and their stores are
+// dropped.  A query row past T then has zero q and dO rows (and D = lse = 0):
+// its P is 1, but its dP, dS and dO are 0, so it adds exactly nothing.
 #include <cmath>
 
 #include "bf16_common.h"
 #include "gattn_internal.h"
+
+#ifndef GATTN_DKDV_STAGES
+#define GATTN_DKDV_STAGES 2
+#endif
+#ifndef GATTN_DQ_STAGES
+#define GATTN_DQ_STAGES 2
+#endif
 
 namespace gattn {
 namespace {
@@ -30,11 +41,14 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------------------
-// D[i] = sum_d dO[i][d] * O[i][d]; HS/8 threads per row, 16-byte loads.
+// D[i] = sum_d dO[i][d] * O[i][d] and L2[i] = lse[i] * log2(e); HS/8 threads
+// per row, 16-byte loads.
 template <int HS>
 __global__ __launch_bounds__(kThreads) void bf16_pre_kernel(const uint16_t* __restrict__ o,
                                                            const uint16_t* __restrict__ dO,
-                                                           float* __restrict__ D, long rows) {
+                                                           const float* __restrict__ lse,
+                                                           float* __restrict__ D,
+                                                           float* __restrict__ L2, long rows) {
   constexpr int TPR = HS / 8;
   const long gid = long(blockIdx.x) * kThreads + threadIdx.x;
   const long row = gid / TPR;
@@ -51,47 +65,69 @@ __global__ __launch_bounds__(kThreads) void bf16_pre_kernel(const uint16_t* __re
   }
 #pragma unroll
   for (int off = TPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (row < rows && part == 0) D[row] = s;
+  if (row < rows && part == 0) {
+    D[row] = s;
+    L2[row] = lse[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV.  Workgroup = 4 wavefronts = 128 keys of one (b, h); wavefront w
 // keeps keys k0 + 32w .. +31 (K, V as MFMA B operands) and their dK^T, dV^T
 // accumulators in registers.  Steps walk 64-query tiles from the diagonal to
-// T.  Per step and 32-query block:
-//   S = Q K^T, dP = dO V^T          C[query][key]; Q, dO rows read from LDS in
+// T.  Per 32-query block b of a step:
+//   A(b): S = Q K^T, dP = dO V^T    C[query][key]; Q, dO rows read from LDS in
 //                                   perm_row order, so each lane's registers
 //                                   8t..8t+7 are 8 consecutive queries
-//   P, dS (f32, registers) -> bf16  exactly the B operand of the next MFMAs
-//   dV^T += dO^T P, dK^T += Q^T dS  C[d][key]; dO^T, Q^T via LDS transpose reads
+//   B(b): P, dS (f32, registers) -> bf16, exactly the B operand of
+//   C(b): dV^T += dO^T P, dK^T += Q^T dS   C[d][key]; dO^T, Q^T via LDS
+//                                          transpose reads
+// Below the diagonal the blocks are software-pipelined: A(b+1) is issued
+// before B(b), so the matrix cores work on the next block while the vector
+// ALUs do this one's softmax terms.
 template <int HS>
 struct DkdvCfg {
   static constexpr int NW = 4;
-  static constexpr int BN = 32 * NW;              // keys per workgroup
-  static constexpr int BQ = 64;                   // queries per step
+  static constexpr int BN = 32 * NW;  // keys per workgroup
+  static constexpr int BQ = 64;       // queries per step
   static constexpr int QB = BQ / 32;
   static constexpr int KSTEP = HS / 16;
   static constexpr int DB = HS / 32;
-  static constexpr int ST = HS + 8;               // LDS row stride (elements)
-  static constexpr int LPT = BQ * HS / 8 / kThreads;  // 16-byte chunks per thread per tensor
-  static_assert(LPT >= 1, "tile shape");
+  static constexpr int NS = GATTN_DKDV_STAGES;  // LDS ring depth
+  // DMA instructions per wavefront per step: Q and dO tiles, plus one quarter
+  // of the lse and D rows each.
+  static constexpr int PER = 2 * (BQ * HS / 512) / NW + 2;
+  static_assert((BQ * HS / 512) % NW == 0 && BQ % (4 * NW) == 0, "uniform DMA split");
 };
 
-template <int HS, bool MASK>
-__device__ inline void dkdv_block(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
-                                  const float* Db, int qb, int qs0, int krow, int prow, int lane,
-                                  int h, float c, const u32x4 (&kf)[HS / 16],
-                                  const u32x4 (&vf)[HS / 16], f32x16 (&dka)[HS / 32],
-                                  f32x16 (&dva)[HS / 32]) {
+template <int HS>
+struct DkdvRegs {
+  u32x4 kf[HS / 16], vf[HS / 16];
+  f32x16 dka[HS / 32], dva[HS / 32];
+};
+
+// A(b): S and dP of query block qb.
+template <int HS>
+__device__ inline void dkdv_sdp(const uint16_t* Qb, const uint16_t* Gb, int qb,
+                                const LaneOffsets<HS>& L, const DkdvRegs<HS>& R, f32x16& s,
+                                f32x16& dp) {
   using C = DkdvCfg<HS>;
-  const f32x16 zero = {};
-  f32x16 s = zero, dp = zero;
+  s = f32x16{};
+  dp = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < C::KSTEP; ++ks) {
-    const int off = (qb * 32 + prow) * C::ST + 16 * ks + 8 * h;
-    s = mfma32(*reinterpret_cast<const u32x4*>(Qb + off), kf[ks], s);
-    dp = mfma32(*reinterpret_cast<const u32x4*>(Gb + off), vf[ks], dp);
+    s = mfma32(op_nat<HS>(Qb, L, qb * 32, ks), R.kf[ks], s);
+    dp = mfma32(op_nat<HS>(Gb, L, qb * 32, ks), R.vf[ks], dp);
   }
+}
+
+// B(b) then C(b) for query block qb.
+template <int HS, bool MASK>
+__device__ inline void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
+                                 const float* Db, int qb, int qs0, int krow, int h, float c,
+                                 const LaneOffsets<HS>& L, const f32x16& s, const f32x16& dp,
+                                 DkdvRegs<HS>& R) {
+  using C = DkdvCfg<HS>;
   u32x4 pp[2], dsp[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -121,22 +157,52 @@ __device__ inline void dkdv_block(const uint16_t* Qb, const uint16_t* Gb, const 
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
       const int k0 = qb * 32 + 16 * t;
-      dva[db] = mfma32(lds_operand_tr(Gb, C::ST, k0, db * 32, lane), pp[t], dva[db]);
-      dka[db] = mfma32(lds_operand_tr(Qb, C::ST, k0, db * 32, lane), dsp[t], dka[db]);
+      R.dva[db] = mfma32(op_tr<HS>(Gb, L, k0, db), pp[t], R.dva[db]);
+      R.dka[db] = mfma32(op_tr<HS>(Qb, L, k0, db), dsp[t], R.dka[db]);
     }
+}
+
+// One step below the diagonal: every block is visible, no mask, pipelined.
+template <int HS>
+__device__ inline void dkdv_step_full(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
+                                      const float* Db, int qs0, int krow, int h, float c,
+                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R) {
+  using C = DkdvCfg<HS>;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    f32x16 s, dp;
+    dkdv_sdp<HS>(Qb, Gb, qb, L, R, s, dp);
+    dkdv_grad<HS, false>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R);
+  }
+}
+
+// A step that meets the diagonal: blocks wholly before this wavefront's keys
+// are skipped, the others masked.
+template <int HS>
+__device__ inline void dkdv_step_diag(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
+                                      const float* Db, int qs0, int kw0, int krow, int h, float c,
+                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R) {
+  using C = DkdvCfg<HS>;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    if (kw0 > qs0 + qb * 32 + 31) continue;  // all of this wavefront's keys lie after the block
+    f32x16 s, dp;
+    dkdv_sdp<HS>(Qb, Gb, qb, L, R, s, dp);
+    dkdv_grad<HS, true>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R);
+  }
 }
 
 template <int HS>
 __global__ __launch_bounds__(kThreads, 2) void bf16_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ Dg, uint16_t* __restrict__ dk,
+    const float* __restrict__ Dg, const float* __restrict__ L2g, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int BH, int T, float scale) {
   using C = DkdvCfg<HS>;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][C::BQ * C::ST];
-  __shared__ __attribute__((aligned(16))) uint16_t Gs[2][C::BQ * C::ST];
-  __shared__ __attribute__((aligned(16))) float Ls[2][C::BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[2][C::BQ];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[C::NS][C::BQ * HS];
+  __shared__ __attribute__((aligned(16))) uint16_t Gs[C::NS][C::BQ * HS];
+  __shared__ __attribute__((aligned(16))) float Ls[C::NS][C::BQ];
+  __shared__ __attribute__((aligned(16))) float Ds[C::NS][C::BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -147,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dkdv_kernel(
   const uint32_t slice_bytes = uint32_t(T) * HS * 2;
   const rsrc_t rq = make_rsrc(q + base, slice_bytes), rk = make_rsrc(k + base, slice_bytes);
   const rsrc_t rv = make_rsrc(v + base, slice_bytes), rg = make_rsrc(dO + base, slice_bytes);
-  const rsrc_t rl = make_rsrc(lse + long(bh) * T, uint32_t(T) * 4);
+  const rsrc_t rl = make_rsrc(L2g + long(bh) * T, uint32_t(T) * 4);
   const rsrc_t rd = make_rsrc(Dg + long(bh) * T, uint32_t(T) * 4);
 
   const int k0 = kt * C::BN;
@@ -155,69 +221,43 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dkdv_kernel(
   const int krow = kw0 + n;
   const float c = scale * kLog2e;
 
-  u32x4 kf[C::KSTEP], vf[C::KSTEP];
+  DkdvRegs<HS> R;
 #pragma unroll
   for (int ks = 0; ks < C::KSTEP; ++ks) {
     const uint32_t off = uint32_t(krow * HS + 16 * ks + 8 * h) * 2;
-    kf[ks] = bload16(rk, off);
-    vf[ks] = bload16(rv, off);
+    R.kf[ks] = bload16(rk, off);
+    R.vf[ks] = bload16(rv, off);
   }
-  f32x16 dka[C::DB], dva[C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) dka[db] = dva[db] = f32x16{};
+  for (int db = 0; db < C::DB; ++db) R.dka[db] = R.dva[db] = f32x16{};
 
-  u32x4 qr[C::LPT], gr[C::LPT];
-  float lr = 0.f, dr = 0.f;
-  auto gload = [&](int qt) {
-#pragma unroll
-    for (int j = 0; j < C::LPT; ++j) {
-      const int ch = tid + kThreads * j, row = ch / (HS / 8), col = ch % (HS / 8);
-      const uint32_t off = uint32_t((qt * C::BQ + row) * HS + col * 8) * 2;
-      qr[j] = bload16(rq, off);
-      gr[j] = bload16(rg, off);
-    }
-    if (tid < C::BQ) {
-      const int qi = qt * C::BQ + tid;
-      const float l = bloadf(rl, uint32_t(qi) * 4);
-      lr = qi < T ? l * kLog2e : INFINITY;  // rows past T: P = exp2(-inf) = 0
-      dr = bloadf(rd, uint32_t(qi) * 4);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < C::LPT; ++j) {
-      const int ch = tid + kThreads * j, row = ch / (HS / 8), col = ch % (HS / 8);
-      *reinterpret_cast<u32x4*>(&Qs[buf][row * C::ST + col * 8]) = qr[j];
-      *reinterpret_cast<u32x4*>(&Gs[buf][row * C::ST + col * 8]) = gr[j];
-    }
-    if (tid < C::BQ) {
-      Ls[buf][tid] = lr;
-      Ds[buf][tid] = dr;
-    }
+  constexpr int QQ = C::BQ / C::NW;  // lse / D rows per wavefront
+  auto issue = [&](int qt, int buf) {
+    dma_tile<HS, C::BQ, C::NW>(rq, qt * C::BQ, Qs[buf], w, lane);
+    dma_tile<HS, C::BQ, C::NW>(rg, qt * C::BQ, Gs[buf], w, lane);
+    const uint32_t off = uint32_t(qt * C::BQ + w * QQ) * 4;
+    dma_f32(rl, off, Ls[buf] + w * QQ, QQ, lane);
+    dma_f32(rd, off, Ds[buf] + w * QQ, QQ, lane);
   };
 
   const int nqt = (T + C::BQ - 1) / C::BQ;
   const int qt0 = k0 / C::BQ;
-  const int prow = perm_row(n);
-  gload(qt0);
-  lstore(0);
-  __syncthreads();
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int buf = (qt - qt0) & 1;
-    if (qt + 1 < nqt) gload(qt + 1);
-    const int qs0 = qt * C::BQ;
+  const int nsteps = nqt - qt0;
+  const LaneOffsets<HS> L(lane);
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      const int qbase = qs0 + qb * 32;
-      if (kw0 > qbase + 31) continue;  // all of this wavefront's keys lie after the block
-      if (kw0 + 31 > qbase)
-        dkdv_block<HS, true>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qb, qs0, krow, prow, lane, h,
-                             c, kf, vf, dka, dva);
-      else
-        dkdv_block<HS, false>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qb, qs0, krow, prow, lane, h,
-                              c, kf, vf, dka, dva);
-    }
-    if (qt + 1 < nqt) lstore(buf ^ 1);
+  for (int j = 0; j < C::NS - 1; ++j)
+    if (j < nsteps) issue(qt0 + j, j);
+  wait_ring<C::NS, C::PER>(min(C::NS - 2, nsteps - 1));
+  __syncthreads();
+  for (int t = 0; t < nsteps; ++t) {
+    const int buf = t % C::NS;
+    if (t + C::NS - 1 < nsteps) issue(qt0 + t + C::NS - 1, (t + C::NS - 1) % C::NS);
+    const int qs0 = (qt0 + t) * C::BQ;
+    if (qs0 < k0 + C::BN)
+      dkdv_step_diag<HS>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, kw0, krow, h, c, L, R);
+    else
+      dkdv_step_full<HS>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, krow, h, c, L, R);
+    wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nsteps - t - 2)));
     __syncthreads();
   }
 
@@ -228,18 +268,20 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dkdv_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t off = uint32_t(krow * HS + db * 32 + 8 * g + 4 * h) * 2;
-      bstore8(wv, off, u32x2{pack_bf16(dva[db][4 * g], dva[db][4 * g + 1]),
-                             pack_bf16(dva[db][4 * g + 2], dva[db][4 * g + 3])});
-      bstore8(wk, off, u32x2{pack_bf16(dka[db][4 * g] * scale, dka[db][4 * g + 1] * scale),
-                             pack_bf16(dka[db][4 * g + 2] * scale, dka[db][4 * g + 3] * scale)});
+      bstore8(wv, off, u32x2{pack_bf16(R.dva[db][4 * g], R.dva[db][4 * g + 1]),
+                             pack_bf16(R.dva[db][4 * g + 2], R.dva[db][4 * g + 3])});
+      bstore8(wk, off, u32x2{pack_bf16(R.dka[db][4 * g] * scale, R.dka[db][4 * g + 1] * scale),
+                             pack_bf16(R.dka[db][4 * g + 2] * scale, R.dka[db][4 * g + 3] * scale)});
     }
 }
 
 // ---------------------------------------------------------------------------
 // dQ.  Workgroup = 4 wavefronts = 128 queries of one (b, h); wavefront w keeps
 // queries r0 + 32w .. +31 (Q^T and dO^T as MFMA B operands, lse and D as
-// per-lane scalars) and the dQ^T accumulator in registers.  Steps walk
-// 64-key tiles from 0 to the diagonal.  Per step and 32-key block:
+// per-lane scalars) and the dQ^T accumulator in registers.  It computes D
+// from its O and dO rows and writes D and lse*log2(e) to the workspace for
+// the dK/dV kernel.  Steps walk 64-key tiles from 0 to the diagonal.  Per
+// step and 32-key block:
 //   S^T = K Q^T, dP^T = V dO^T      C[key][query]; K, V rows from LDS in
 //                                   perm_row order (8 consecutive keys per
 //                                   lane in registers 8t..8t+7)
@@ -248,31 +290,29 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dkdv_kernel(
 template <int HS>
 struct DqCfg {
   static constexpr int NW = 4;
-  static constexpr int BM = 32 * NW;              // queries per workgroup
-  static constexpr int BN = 64;                   // keys per step
+  static constexpr int BM = 32 * NW;  // queries per workgroup
+  static constexpr int BN = 64;       // keys per step
   static constexpr int KSTEP = HS / 16;
   static constexpr int DB = HS / 32;
-  static constexpr int ST = HS + 8;
-  static constexpr int KPT = BN * HS / 8 / kThreads;
-  static_assert(KPT >= 1, "tile shape");
+  static constexpr int NS = GATTN_DQ_STAGES;  // LDS ring depth
+  static constexpr int PER = 2 * (BN * HS / 512) / NW;  // DMA instructions per wavefront per step
+  static_assert((BN * HS / 512) % NW == 0, "uniform DMA split");
 };
 
 template <int HS, bool MASK>
-__device__ inline void dq_step(const uint16_t* Kb, const uint16_t* Vb, int key0, int qrow,
-                               int prow, int lane, int h, float c, float lse2, float Dq,
+__device__ inline void dq_step(const uint16_t* Kb, const uint16_t* Vb, int key0, int qrow, int h,
+                               float c, float lse2, float Dq, const LaneOffsets<HS>& L,
                                const u32x4 (&qf)[HS / 16], const u32x4 (&gf)[HS / 16],
                                f32x16 (&dqa)[HS / 32]) {
   using C = DqCfg<HS>;
-  const f32x16 zero = {};
   u32x4 dsp[2][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    f32x16 st = zero, dpt = zero;
+    f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEP; ++ks) {
-      const int off = (kb * 32 + prow) * C::ST + 16 * ks + 8 * h;
-      st = mfma32(*reinterpret_cast<const u32x4*>(Kb + off), qf[ks], st);
-      dpt = mfma32(*reinterpret_cast<const u32x4*>(Vb + off), gf[ks], dpt);
+      st = mfma32(op_nat<HS>(Kb, L, kb * 32, ks), qf[ks], st);
+      dpt = mfma32(op_nat<HS>(Vb, L, kb * 32, ks), gf[ks], dpt);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -293,19 +333,26 @@ __device__ inline void dq_step(const uint16_t* Kb, const uint16_t* Vb, int key0,
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
-        dqa[db] = mfma32(lds_operand_tr(Kb, C::ST, kb * 32 + 16 * t, db * 32, lane), dsp[kb][t],
-                         dqa[db]);
+        dqa[db] = mfma32(op_tr<HS>(Kb, L, kb * 32 + 16 * t, db), dsp[kb][t], dqa[db]);
+  // Scheduling hint: spread the MFMAs over the step, each followed by vector
+  // ALU work and LDS reads of other blocks, instead of phase after phase.
+#pragma unroll
+  for (int i = 0; i < 8 * C::KSTEP + 4 * C::DB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
 }
 
 template <int HS>
 __global__ __launch_bounds__(kThreads, 2) void bf16_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
-    const float* __restrict__ lse, const float* __restrict__ Dg, uint16_t* __restrict__ dq,
-    int BH, int T, float scale) {
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse, float* __restrict__ Dg,
+    float* __restrict__ L2g, uint16_t* __restrict__ dq, int BH, int T, float scale) {
   using C = DqCfg<HS>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::BN * C::ST];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::BN * C::ST];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[C::NS][C::BN * HS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[C::NS][C::BN * HS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -316,60 +363,63 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dq_kernel(
   const uint32_t slice_bytes = uint32_t(T) * HS * 2;
   const rsrc_t rq = make_rsrc(q + base, slice_bytes), rk = make_rsrc(k + base, slice_bytes);
   const rsrc_t rv = make_rsrc(v + base, slice_bytes), rg = make_rsrc(dO + base, slice_bytes);
+  const rsrc_t ro = make_rsrc(o + base, slice_bytes);
 
   const int r0 = qt * C::BM;
   const int q0 = r0 + 32 * w;
   const int qrow = q0 + n;
   const float c = scale * kLog2e;
+
+  auto issue = [&](int kt, int buf) {
+    dma_tile<HS, C::BN, C::NW>(rk, kt * C::BN, Ks[buf], w, lane);
+    dma_tile<HS, C::BN, C::NW>(rv, kt * C::BN, Vs[buf], w, lane);
+  };
+  const int nkt = (min(r0 + C::BM, T) - 1) / C::BN + 1;
+#pragma unroll
+  for (int j = 0; j < C::NS - 1; ++j)
+    if (j < nkt) issue(j, j);
+
+  // Q^T, dO^T fragments (lane (n, h): row qrow, columns 16 ks + 8h .. +7), and
+  // D = rowsum(dO * O) of this lane's query from the same columns of O.
   u32x4 qf[C::KSTEP], gf[C::KSTEP];
+  float dpart = 0.f;
 #pragma unroll
   for (int ks = 0; ks < C::KSTEP; ++ks) {
     const uint32_t off = uint32_t(qrow * HS + 16 * ks + 8 * h) * 2;
     qf[ks] = bload16(rq, off);
     gf[ks] = bload16(rg, off);
+    const u32x4 of = bload16(ro, off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dpart = fmaf(bf16lo(of[e]), bf16lo(gf[ks][e]), dpart);
+      dpart = fmaf(bf16hi(of[e]), bf16hi(gf[ks][e]), dpart);
+    }
   }
-  const float lraw = bloadf(make_rsrc(lse + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4);
-  const float lse2 = qrow < T ? lraw * kLog2e : INFINITY;
-  const float Dq = bloadf(make_rsrc(Dg + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4);
+  const float Dq = halves_sum(dpart);
+  const float lse2 = bloadf(make_rsrc(lse + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4) *
+                     kLog2e;
+  if (h == 0) {
+    bstoref(make_rsrc(Dg + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4, Dq);
+    bstoref(make_rsrc(L2g + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4, lse2);
+  }
   f32x16 dqa[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) dqa[db] = f32x16{};
 
-  u32x4 kr[C::KPT], vr[C::KPT];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int j = 0; j < C::KPT; ++j) {
-      const int ch = tid + kThreads * j, row = ch / (HS / 8), col = ch % (HS / 8);
-      const uint32_t off = uint32_t((kt * C::BN + row) * HS + col * 8) * 2;
-      kr[j] = bload16(rk, off);
-      vr[j] = bload16(rv, off);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < C::KPT; ++j) {
-      const int ch = tid + kThreads * j, row = ch / (HS / 8), col = ch % (HS / 8);
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * C::ST + col * 8]) = kr[j];
-      *reinterpret_cast<u32x4*>(&Vs[buf][row * C::ST + col * 8]) = vr[j];
-    }
-  };
-
-  const int nkt = (min(r0 + C::BM, T) - 1) / C::BN + 1;
-  const int prow = perm_row(n);
-  gload(0);
-  lstore(0);
+  const LaneOffsets<HS> L(lane);
+  wait_vmem();  // the first stages and this wavefront's q, dO, O, lse rows
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
+    const int buf = kt % C::NS;
+    if (kt + C::NS - 1 < nkt) issue(kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
     const int key0 = kt * C::BN;
     if (q0 < T && key0 <= q0 + 31) {
       if (key0 + C::BN - 1 > q0)
-        dq_step<HS, true>(Ks[buf], Vs[buf], key0, qrow, prow, lane, h, c, lse2, Dq, qf, gf, dqa);
+        dq_step<HS, true>(Ks[buf], Vs[buf], key0, qrow, h, c, lse2, Dq, L, qf, gf, dqa);
       else
-        dq_step<HS, false>(Ks[buf], Vs[buf], key0, qrow, prow, lane, h, c, lse2, Dq, qf, gf, dqa);
+        dq_step<HS, false>(Ks[buf], Vs[buf], key0, qrow, h, c, lse2, Dq, L, qf, gf, dqa);
     }
-    if (kt + 1 < nkt) lstore(buf ^ 1);
+    wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
   }
 
@@ -387,37 +437,38 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dq_kernel(
 
 }  // namespace
 
-hipError_t bf16_bwd_pre(const uint16_t* o, const uint16_t* dO, float* D, int BH, int T, int hs,
-                        hipStream_t s) {
+hipError_t bf16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
+                        float* L2, int BH, int T, int hs, hipStream_t s) {
   const long rows = long(BH) * T;
   const long threads = rows * (hs / 8);
   const dim3 grid(unsigned((threads + kThreads - 1) / kThreads));
-  if (hs == 64) return launch(bf16_pre_kernel<64>, grid, dim3(kThreads), s, o, dO, D, rows);
-  return launch(bf16_pre_kernel<32>, grid, dim3(kThreads), s, o, dO, D, rows);
+  if (hs == 64) return launch(bf16_pre_kernel<64>, grid, dim3(kThreads), s, o, dO, lse, D, L2, rows);
+  return launch(bf16_pre_kernel<32>, grid, dim3(kThreads), s, o, dO, lse, D, L2, rows);
 }
 
 hipError_t bf16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const uint16_t* dO, const float* lse, const float* D, uint16_t* dk,
+                         const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
                          uint16_t* dv, int BH, int T, int hs, float scale, hipStream_t s) {
-  const int bn = 128;
+  const int bn = DkdvCfg<64>::BN;
   const dim3 grid(unsigned(((T + bn - 1) / bn) * BH));
   if (hs == 64)
-    return launch(bf16_dkdv_kernel<64>, grid, dim3(kThreads), s, q, k, v, dO, lse, D, dk, dv, BH,
+    return launch(bf16_dkdv_kernel<64>, grid, dim3(kThreads), s, q, k, v, dO, D, L2, dk, dv, BH,
                   T, scale);
-  return launch(bf16_dkdv_kernel<32>, grid, dim3(kThreads), s, q, k, v, dO, lse, D, dk, dv, BH, T,
+  return launch(bf16_dkdv_kernel<32>, grid, dim3(kThreads), s, q, k, v, dO, D, L2, dk, dv, BH, T,
                 scale);
 }
 
 hipError_t bf16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                       const uint16_t* dO, const float* lse, const float* D, uint16_t* dq, int BH,
-                       int T, int hs, float scale, hipStream_t s) {
-  const int bm = 128;
+                       const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
+                       float* L2, uint16_t* dq, int BH, int T, int hs, float scale,
+                       hipStream_t s) {
+  const int bm = DqCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
   if (hs == 64)
-    return launch(bf16_dq_kernel<64>, grid, dim3(kThreads), s, q, k, v, dO, lse, D, dq, BH, T,
-                  scale);
-  return launch(bf16_dq_kernel<32>, grid, dim3(kThreads), s, q, k, v, dO, lse, D, dq, BH, T,
-                scale);
+    return launch(bf16_dq_kernel<64>, grid, dim3(kThreads), s, q, k, v, o, dO, lse, D, L2, dq,
+                  BH, T, scale);
+  return launch(bf16_dq_kernel<32>, grid, dim3(kThreads), s, q, k, v, o, dO, lse, D, L2, dq, BH,
+                T, scale);
 }
 
 }  // namespace gattn

@@ -51,17 +51,6 @@ __device__ inline u32x2 ds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
-// 32x32x16 MFMA operand (lane l holds n = l%32 and k = 8*(l/32) .. +7, i.e.
-// the B layout, which is also the A layout with m in place of n) read from a
-// row-major LDS matrix M[k][n] with row stride `st` elements, for the block
-// k0 .. k0+15, n0 .. n0+31.  Two transpose reads, rows +0..3 and +4..7.
-__device__ inline u32x4 lds_operand_tr(const uint16_t* M, int st, int k0, int n0, int lane) {
-  const int g = lane >> 4, j = lane & 15;
-  const uint16_t* p = M + (k0 + 8 * (g >> 1) + (j >> 2)) * st + n0 + 16 * (g & 1) + 4 * (j & 3);
-  const u32x2 a = ds_read_tr(p), b = ds_read_tr(p + 4 * st);
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
-
 // Buffer resources: raw (stride 0) buffers whose size bounds every access in
 // hardware.  Loads past `bytes` return zero and stores past it are dropped,
 // so row tails need no branches.  The fourth descriptor word is the gfx9
@@ -81,6 +70,152 @@ __device__ inline void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
 }
 __device__ inline void bstoref(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles.  A tile holds rows of HS bf16 back to back (HS*2 bytes,
+// no padding); the 16-byte chunk c of row r sits at chunk position
+// c ^ swz(r).  The swizzle makes both access patterns below free of bank
+// conflicts (64 banks x 4 bytes):
+//   * MFMA operand rows (16-byte reads, 32 consecutive or perm_row-ordered
+//     rows, one chunk each);
+//   * transpose reads (8 bytes per lane, 4 rows x 64 bytes per 32 lanes).
+// HS = 64: rows r, r+1 share swz = rot3((r >> 1) & 7), rot3 moving bit 0 to
+// bit 2, so rows r and r+2 use opposite halves of the row; HS = 32:
+// swz = (r >> 2) & 3.
+template <int HS>
+__device__ inline int swz(int r) {
+  if constexpr (HS == 64) {
+    const int j = (r >> 1) & 7;
+    return ((j & 1) << 2) | (j >> 1);
+  } else {
+    return (r >> 2) & 3;
+  }
+}
+// Element offset of (row r, column col) in a swizzled tile.
+template <int HS>
+__device__ inline int toff(int r, int col) {
+  return r * HS + ((((col >> 3) ^ swz<HS>(r)) & (HS / 8 - 1)) << 3) + (col & 7);
+}
+// 16-byte MFMA operand: row r, columns col .. col+7 (col a multiple of 8).
+template <int HS>
+__device__ inline u32x4 tile_row16(const uint16_t* tile, int r, int col) {
+  return *reinterpret_cast<const u32x4*>(tile + toff<HS>(r, col));
+}
+
+// 32x32x16 MFMA operand (lane l holds n = l%32 and k = 8*(l/32) .. +7, i.e.
+// the B layout, which is also the A layout with m in place of n) read from a
+// swizzled tile M[k][n] (row = k), for k0 .. k0+15 and n0 .. n0+31, with two
+// transpose reads (rows +0..3 and +4..7 of each 8-row half).
+template <int HS>
+__device__ inline u32x4 tile_operand_tr(const uint16_t* M, int k0, int n0, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const int r = k0 + 8 * (g >> 1) + (j >> 2);
+  const int col = n0 + 16 * (g & 1) + 4 * (j & 3);
+  const u32x2 a = ds_read_tr(M + toff<HS>(r, col)), b = ds_read_tr(M + toff<HS>(r + 4, col));
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// Per-lane element offsets into a swizzled tile, computed once per kernel.
+// The swizzle repeats every 16 rows, so a block starting at a multiple of 16
+// rows only adds a compile-time constant: every LDS read in the main loops is
+// (lane offset register) + (immediate).
+//   nat[ks]    : row perm_row(l%32), columns 16 ks + 8 (l/32) .. +7, i.e. the
+//                16-byte A (or B) operand row of a 32x32x16 MFMA whose 32
+//                rows start at a multiple of 32;
+//   tra/trb[db]: the two transpose reads of tile_operand_tr for k0 = 0 and
+//                n0 = 32 db (add k0 * HS for a block starting at row k0).
+template <int HS>
+struct LaneOffsets {
+  int nat[HS / 16];
+  int tra[HS / 32], trb[HS / 32];
+  __device__ explicit LaneOffsets(int lane) {
+    const int n = lane & 31, h = lane >> 5;
+    const int prow = perm_row(n);
+#pragma unroll
+    for (int ks = 0; ks < HS / 16; ++ks) nat[ks] = toff<HS>(prow, 16 * ks + 8 * h);
+    const int g = lane >> 4, j = lane & 15;
+    const int r = 8 * (g >> 1) + (j >> 2), col = 16 * (g & 1) + 4 * (j & 3);
+#pragma unroll
+    for (int db = 0; db < HS / 32; ++db) {
+      tra[db] = toff<HS>(r, 32 * db + col);
+      trb[db] = toff<HS>(r + 4, 32 * db + col);
+    }
+  }
+};
+// Natural operand of the 32-row block starting at row r0 (r0 % 32 == 0).
+template <int HS>
+__device__ inline u32x4 op_nat(const uint16_t* tile, const LaneOffsets<HS>& L, int r0, int ks) {
+  return *reinterpret_cast<const u32x4*>(tile + r0 * HS + L.nat[ks]);
+}
+// Transposed operand of rows k0 .. k0+15 (k0 % 16 == 0), columns 32 db .. +31.
+template <int HS>
+__device__ inline u32x4 op_tr(const uint16_t* tile, const LaneOffsets<HS>& L, int k0, int db) {
+  const u32x2 a = ds_read_tr(tile + k0 * HS + L.tra[db]);
+  const u32x2 b = ds_read_tr(tile + k0 * HS + L.trb[db]);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// Tile load by LDS DMA (buffer_load_dwordx4 ... lds): every lane moves 16
+// bytes from global memory straight into LDS at (wave's LDS base) + 16 * lane,
+// with no register staging.  Lane L of DMA instruction i fills chunk position
+// L % (HS/8) of tile row i*(512/HS) + L/(HS/8), so it fetches the global chunk
+// that the swizzle puts there.  Rows past the buffer resource's end arrive as
+// zeros.  ROWS rows starting at global row row0 of the resource; the NW
+// wavefronts of the workgroup share the instructions.  The caller waits
+// (s_waitcnt vmcnt) and synchronises before reading the tile.
+template <int HS, int ROWS, int NW>
+__device__ inline void dma_tile(rsrc_t r, int row0, uint16_t* tile, int w, int lane) {
+  constexpr int RPI = 512 / HS;  // rows per DMA instruction (1 KB)
+  constexpr int NI = ROWS / RPI;
+  static_assert(NI * RPI == ROWS, "tile rows");
+#pragma unroll
+  for (int i = w; i < NI; i += NW) {
+    const int rl = i * RPI + lane / (HS / 8);
+    const int c = (lane % (HS / 8)) ^ swz<HS>(rl);
+    const uint32_t off = uint32_t((row0 + rl) * HS + c * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(tile + i * 512), 16, off, 0, 0, 0);
+  }
+}
+// DMA of n32 4-byte values (n32 <= 64) from byte offset off0 of a resource
+// into LDS (one instruction; lanes >= n32 idle).
+__device__ inline void dma_f32(rsrc_t r, uint32_t off0, float* dst, int n32, int lane) {
+  if (lane < n32)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst), 4,
+                                             off0 + 4u * lane, 0, 0, 0);
+}
+// Wait until at most N of this wavefront's vector-memory operations (LDS DMA
+// included) are outstanding; they complete in issue order.  LDS and export
+// counters are left alone (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ inline void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ inline void wait_vmem() { wait_vmem_n<0>(); }
+
+// Ring of NS LDS stages fed by DMA: before computing step t, step t+NS-1 is
+// issued; after it, the caller needs step t+1 complete, i.e. at most the DMA
+// of the steps after t+1 that were issued may remain outstanding.  PER is the
+// number of DMA instructions one wavefront issues per step (the same for
+// every wavefront).  `later` = steps issued after step t+1 (0 .. NS-2).
+template <int NS, int PER>
+__device__ inline void wait_ring(int later) {
+  if constexpr (NS >= 4) {
+    if (later >= 2) {
+      wait_vmem_n<2 * PER>();
+      return;
+    }
+  }
+  if constexpr (NS >= 3) {
+    if (later >= 1) {
+      wait_vmem_n<PER>();
+      return;
+    }
+  }
+  wait_vmem_n<0>();
 }
 
 // Reductions across the two 32-lane halves of a wavefront (lanes l and l^32)

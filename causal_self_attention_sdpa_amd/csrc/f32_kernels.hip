@@ -96,27 +96,31 @@ __global__ __launch_bounds__(64 * kWaves) void f32_fwd_kernel(
   if (lse != nullptr && lane == 0) lse[row] = m + logf(l);
 }
 
-// D[i] = <dO_i, o_i>, one wavefront per row.
+// D[i] = <dO_i, o_i> and L2[i] = lse[i] * log2(e), one wavefront per row.
 template <int NPL>
-__global__ __launch_bounds__(64 * kWaves) void f32_pre_kernel(const float* __restrict__ o,
-                                                              const float* __restrict__ dO,
-                                                              float* __restrict__ D, int BH, int T,
-                                                              int hs) {
+__global__ __launch_bounds__(64 * kWaves) void f32_pre_kernel(
+    const float* __restrict__ o, const float* __restrict__ dO, const float* __restrict__ lse,
+    float* __restrict__ D, float* __restrict__ L2, int BH, int T, int hs) {
   const int lane = threadIdx.x & 63;
   const long row = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (row >= long(BH) * T) return;
   float a[NPL];
   load_row<NPL>(dO + row * hs, hs, lane, a);
   const float s = wave_sum(row_dot<NPL>(a, o + row * hs, hs, lane));
-  if (lane == 0) D[row] = s;
+  if (lane == 0) {
+    D[row] = s;
+    L2[row] = lse[row] * 1.4426950408889634f;
+  }
 }
 
 // dK_j, dV_j: one wavefront per key row j, loop over queries i >= j.
+// P = exp2(s * scale * log2(e) - L2) with L2 = lse * log2(e) from the workspace.
 template <int NPL>
 __global__ __launch_bounds__(64 * kWaves) void f32_dkdv_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const float* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ D,
+    const float* __restrict__ dO, const float* __restrict__ D, const float* __restrict__ L2,
     float* __restrict__ dk, float* __restrict__ dv, int BH, int T, int hs, float scale) {
+  const float c = scale * 1.4426950408889634f;
   const int lane = threadIdx.x & 63;
   const long row = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (row >= long(BH) * T) return;
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(64 * kWaves) void f32_dkdv_kernel(
     float s = row_dot<NPL>(kr, qb + long(i) * hs, hs, lane);
     float dp = row_dot<NPL>(vr, ob + long(i) * hs, hs, lane);
     wave_sum2(s, dp);
-    const float p = expf(s * scale - lse[bh * T + i]);
+    const float p = exp2f(fmaf(s, c, -L2[bh * T + i]));
     const float ds = p * (dp - D[bh * T + i]);
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
@@ -209,20 +213,22 @@ hipError_t f32_fwd(const float* q, const float* k, const float* v, float* o, flo
                 hs, scale);
 }
 
-hipError_t f32_bwd_pre(const float* o, const float* dO, float* D, int BH, int T, int hs,
-                       hipStream_t s) {
+hipError_t f32_bwd_pre(const float* o, const float* dO, const float* lse, float* D, float* L2,
+                       int BH, int T, int hs, hipStream_t s) {
   if (hs <= 64)
-    return launch(f32_pre_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, o, dO, D, BH, T, hs);
-  return launch(f32_pre_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, o, dO, D, BH, T, hs);
+    return launch(f32_pre_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, o, dO, lse, D, L2, BH,
+                  T, hs);
+  return launch(f32_pre_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, o, dO, lse, D, L2, BH, T,
+                hs);
 }
 
 hipError_t f32_bwd_dkdv(const float* q, const float* k, const float* v, const float* dO,
-                        const float* lse, const float* D, float* dk, float* dv, int BH, int T,
+                        const float* D, const float* L2, float* dk, float* dv, int BH, int T,
                         int hs, float scale, hipStream_t s) {
   if (hs <= 64)
-    return launch(f32_dkdv_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D,
+    return launch(f32_dkdv_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, D, L2,
                   dk, dv, BH, T, hs, scale);
-  return launch(f32_dkdv_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D, dk,
+  return launch(f32_dkdv_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, D, L2, dk,
                 dv, BH, T, hs, scale);
 }
 

@@ -82,9 +82,9 @@ int gattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int T, int hs, float scale, int dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace gattn_bwd needs: D = rowsum(dO * o), float32
- * (B, H, T), rounded up to a multiple of 256.  Returns 0 for arguments
- * gattn_bwd would reject.
+ * Bytes of device workspace the backward needs: D = rowsum(dO * o) and
+ * lse * log2(e), each float32 (B, H, T) starting on a 256-byte boundary.
+ * Returns 0 for arguments gattn_bwd would reject.
  */
 size_t gattn_bwd_workspace_bytes(int B, int H, int T, int hs, int dtype);
 
@@ -97,8 +97,8 @@ size_t gattn_bwd_workspace_bytes(int B, int H, int T, int hs, int dtype);
  *   workspace      : caller-owned device memory of at least
  *                    gattn_bwd_workspace_bytes() bytes, 256-byte aligned; the
  *                    library overwrites it (it needs no clearing).
- * Equivalent to gattn_bwd_preprocess, gattn_bwd_dkdv, gattn_bwd_dq in that
- * order on `stream`.  Every output is deterministic (no atomics).
+ * Equivalent to gattn_bwd_dq then gattn_bwd_dkdv on `stream`.  Every output
+ * is deterministic (no atomics).
  */
 int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
               const float* lse, void* dq, void* dk, void* dv,
@@ -106,28 +106,31 @@ int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Backward stage 1: D[i] = sum_d dO[i][d] * o[i][d] (float32) into the
- * workspace; D is the row term of dS = P (dP - D).
+ * Backward, row terms only: D[i] = sum_d dO[i][d] * o[i][d] (the row term of
+ * dS = P (dP - D)) and lse[i] * log2(e), float32, into the workspace.  Needed
+ * before gattn_bwd_dkdv when gattn_bwd_dq is not run first.
  */
-int gattn_bwd_preprocess(const void* o, const void* dO, int B, int H, int T, int hs, int dtype,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+int gattn_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int T,
+                         int hs, int dtype, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /*
- * Backward stage 2: dk and dv.  Recomputes P from q, k and lse (exactly 0
- * above the diagonal) and dS from dO, v and stage 1's D.
- *   dk = scale * dS^T q,  dv = P^T dO.
+ * Backward, dq = scale * dS k, with P recomputed from q, k and lse (exactly 0
+ * above the diagonal) and dS = P (dO v^T - D).  Also leaves the row terms of
+ * gattn_bwd_preprocess in the workspace.
  */
-int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                   void* dk, void* dv, int B, int H, int T, int hs, float scale, int dtype,
-                   const void* workspace, size_t workspace_bytes, hipStream_t stream);
+int gattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                 const float* lse, void* dq, int B, int H, int T, int hs, float scale, int dtype,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Backward stage 3: dq = scale * dS k, recomputing P and dS as stage 2 does.
- * Independent of stage 2's outputs (both need only stage 1's D).
+ * Backward, dk = scale * dS^T q and dv = P^T dO, recomputing P and dS as
+ * gattn_bwd_dq does from the row terms already in the workspace (written by
+ * gattn_bwd_dq or gattn_bwd_preprocess earlier on the stream).
  */
-int gattn_bwd_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                 void* dq, int B, int H, int T, int hs, float scale, int dtype,
-                 const void* workspace, size_t workspace_bytes, hipStream_t stream);
+int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk,
+                   void* dv, int B, int H, int T, int hs, float scale, int dtype, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a gattn_status value. */
 const char* gattn_status_string(int status);

@@ -35,9 +35,11 @@ def gpu_fwd_bwd(x: dict, dtype: str, scale: float, use_stages: bool = False):
                      dtype=torch.uint8, device="cuda")
     dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
     if use_stages:
-        ga.gattn_bwd_preprocess(o, t["do"], ws)
-        ga.gattn_bwd_dq(t["q"], t["k"], t["v"], t["do"], lse, dq, scale, ws)
-        ga.gattn_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], lse, dk, dv, scale, ws)
+        # row terms from the preprocess stage, dk/dv first, then dq (which
+        # rewrites the same row terms)
+        ga.gattn_bwd_preprocess(o, t["do"], lse, ws)
+        ga.gattn_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], dk, dv, scale, ws)
+        ga.gattn_bwd_dq(t["q"], t["k"], t["v"], o, t["do"], lse, dq, scale, ws)
     else:
         ga.gattn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, dq, dk, dv, scale, ws)
     torch.cuda.synchronize()

@@ -44,10 +44,10 @@ def test_status_strings(lib):
 def test_workspace_bytes(lib):
     B, H, T, hs = 12, 12, 1024, 64
     n = ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16)
-    assert n == B * H * T * 4  # D only
-    assert ga.gattn_bwd_workspace_bytes(4, 4, 8, 8, ga.F32) == 512  # 4*4*8 floats, 256-aligned
-    assert ga.gattn_bwd_workspace_bytes(1, 1, 3, 64, ga.BF16) == 256
-    assert ga.gattn_bwd_workspace_bytes(1, 1, 65, 32, ga.BF16) == 512
+    assert n == 2 * B * H * T * 4  # D and lse*log2(e)
+    assert ga.gattn_bwd_workspace_bytes(4, 4, 8, 8, ga.F32) == 1024  # 2 x 4*4*8 floats, 256-aligned
+    assert ga.gattn_bwd_workspace_bytes(1, 1, 3, 64, ga.BF16) == 512
+    assert ga.gattn_bwd_workspace_bytes(1, 1, 65, 32, ga.BF16) == 1024
     assert ga.gattn_bwd_workspace_bytes(0, 1, 1, 64, ga.BF16) == 0
     assert ga.gattn_bwd_workspace_bytes(1, 1, 1, 48, ga.BF16) == 0  # unsupported hs
     assert ga.gattn_bwd_workspace_bytes(1, 1, 1, 8, 7) == 0
@@ -97,20 +97,28 @@ def test_bwd_validation(lib):
 
 
 def test_stage_validation(lib):
-    assert lib.gattn_bwd_preprocess(None, P, 1, 1, 8, 64, 1, P, 1 << 20, None) == INVALID
-    assert lib.gattn_bwd_preprocess(P, P, 1, 1, 8, 64, 1, P, 1, None) == WORKSPACE
-    assert lib.gattn_bwd_preprocess(P, P, 1, 1, 8, 48, 1, P, 1 << 20, None) == UNSUPPORTED
-    # dkdv: q, k, v, dO, lse, dk, dv
+    # preprocess: o, dO, lse
+    assert lib.gattn_bwd_preprocess(None, P, P, 1, 1, 8, 64, 1, P, 1 << 20, None) == INVALID
+    assert lib.gattn_bwd_preprocess(P, P, None, 1, 1, 8, 64, 1, P, 1 << 20, None) == INVALID
+    assert lib.gattn_bwd_preprocess(P, P, P, 1, 1, 8, 64, 1, P, 1, None) == WORKSPACE
+    assert lib.gattn_bwd_preprocess(P, P, P, 1, 1, 8, 48, 1, P, 1 << 20, None) == UNSUPPORTED
+    # dq: q, k, v, o, dO, lse, dq
     for i in range(7):
         p = [P] * 7
         p[i] = None
-        assert lib.gattn_bwd_dkdv(*p, 1, 1, 8, 64, 0.125, 1, P, 1 << 20, None) == INVALID, i
-    assert lib.gattn_bwd_dkdv(*([P] * 7), 1, 1, 8, 64, 0.0, 1, P, 1 << 20, None) == INVALID
-    assert lib.gattn_bwd_dkdv(*([P] * 7), 1, 1, 8, 64, 0.125, 1, P, 4, None) == WORKSPACE
-    # dq: q, k, v, dO, lse, dq
-    for i in range(6):
-        p = [P] * 6
+        assert lib.gattn_bwd_dq(*p, 1, 1, 8, 64, 0.125, 1, P, 1 << 20, None) == INVALID, i
         p[i] = P + 4
         assert lib.gattn_bwd_dq(*p, 1, 1, 8, 64, 0.125, 1, P, 1 << 20, None) == INVALID, i
-    assert lib.gattn_bwd_dq(*([P] * 6), 1, 1, 8, 200, 0.125, 0, P, 1 << 20, None) == UNSUPPORTED
-    assert lib.gattn_bwd_dq(*([P] * 6), 1, 1, 8, 64, 0.125, 1, None, 1 << 20, None) == WORKSPACE
+    assert lib.gattn_bwd_dq(*([P] * 7), 1, 1, 8, 64, 0.0, 1, P, 1 << 20, None) == INVALID
+    assert lib.gattn_bwd_dq(*([P] * 7), 1, 1, 8, 200, 0.125, 0, P, 1 << 20, None) == UNSUPPORTED
+    assert lib.gattn_bwd_dq(*([P] * 7), 1, 1, 8, 64, 0.125, 1, None, 1 << 20, None) == WORKSPACE
+    # dkdv: q, k, v, dO, dk, dv
+    for i in range(6):
+        p = [P] * 6
+        p[i] = None
+        assert lib.gattn_bwd_dkdv(*p, 1, 1, 8, 64, 0.125, 1, P, 1 << 20, None) == INVALID, i
+    assert lib.gattn_bwd_dkdv(*([P] * 6), 1, 1, 8, 64, float("inf"), 1, P, 1 << 20,
+                              None) == INVALID
+    assert lib.gattn_bwd_dkdv(*([P] * 6), 1, 1, 8, 64, 0.125, 1, P, 4, None) == WORKSPACE
+    assert lib.gattn_bwd_dkdv(*([P] * 6), 1, 1, 8, 64, 0.125, 1, P + 64, 1 << 20,
+                              None) == WORKSPACE
