@@ -7,22 +7,25 @@
 // independent (1:22:27).  The per-row log-sum-exp is written for the backward.
 //
 // Work split: one workgroup = 4 wavefronts = 128 query rows of one (b, h);
-// wavefront w owns rows r0 + 32w .. r0 + 32w + 31.  Key/value tiles of 64
-// rows stream through LDS; tiles entirely above the diagonal are never loaded.
-// Per tile and wavefront:
+// wavefront w owns rows r0 + 32w .. r0 + 32w + 31.  64-row key and value
+// tiles arrive in double-buffered, swizzled LDS tiles by LDS DMA; tiles
+// entirely above the diagonal are never loaded.  Per tile and wavefront:
 //   S^T (keys x queries) = K Q^T   on MFMA, Q^T held in registers for the
-//                                   whole loop (B operand), K read from LDS;
-//   online softmax in base 2 (running max m, running sum l, per query =
-//   per lane, so the rescale factor is a per-lane scalar);
+//                                   whole loop (B operand), K rows read from
+//                                   LDS in perm_row order so each lane's
+//                                   registers 8t..8t+7 are 8 consecutive keys;
+//   online softmax in base 2 (running max m and sum l per query = per lane,
+//   so the rescale factor is a per-lane scalar).  A row's reference max m
+//   only moves when the row's maximum exceeds it by more than 2^8 in the
+//   base-2 domain, so the weights stay <= 256 (well inside bf16 and float32 range)
+//   and the output is rescaled only on those rare tiles;
 //   O^T (hs x queries) += V^T P^T  on MFMA, P^T straight from the S^T
 //                                   accumulators (no LDS round trip), V^T
-//                                   read from LDS.
-// K rows are fed to the MFMA A operand in a permuted order (bits 2 and 3 of
-// the row index swapped) so that each lane's 8 consecutive accumulator
-// registers hold 8 consecutive keys: exactly the B-operand layout of the
-// second MFMA.  V is transposed on its way into LDS (register pair swizzle),
-// so both MFMAs read 16-byte LDS vectors.  Global loads for tile t+1 are
-// issued before tile t is computed.
+//                                   read from the row-major V tile with LDS
+//                                   transpose reads.
+// Rows past T are read as zeros (buffer resources sized to one (b, h)
+// slice); keys past T are always above the diagonal of every real query, so
+// the mask removes them, and stores of rows past T are dropped.
 #include <cmath>
 
 #include "bf16_common.h"
@@ -31,30 +34,99 @@
 namespace gattn {
 namespace {
 
+constexpr int kThreads = 256;
+
 template <int HS>
 struct FwdCfg {
-  static constexpr int NW = 4;              // wavefronts per workgroup
-  static constexpr int BM = 32 * NW;        // query rows per workgroup
-  static constexpr int BN = 64;             // key rows per tile
-  static constexpr int KST = HS + 8;        // LDS row stride of K (elements)
-  static constexpr int VST = BN + 8;        // LDS row stride of V^T (elements)
-  static constexpr int KSTEP = HS / 16;     // MFMA k-steps over hs
-  static constexpr int DB = HS / 32;        // 32-wide blocks of hs
-  static constexpr int KPT = BN * HS / 8 / (64 * NW);  // 16-byte K chunks per thread
-  static constexpr int VU = (BN / 8) * (HS / 2);        // V transpose units (8 keys x 2 d)
-  static_assert(KPT >= 1 && VU % 64 == 0 && VU <= 64 * NW, "tile shape");
+  static constexpr int NW = 4;            // wavefronts per workgroup
+  static constexpr int BM = 32 * NW;      // query rows per workgroup
+  static constexpr int BN = 64;           // key rows per tile
+  static constexpr int KSTEP = HS / 16;   // MFMA k-steps over hs
+  static constexpr int DB = HS / 32;      // 32-wide blocks of hs
+  static_assert((BN * HS / 512) % NW == 0, "uniform DMA split");
 };
 
 template <int HS>
-__global__ __launch_bounds__(256) void bf16_fwd_kernel(const uint16_t* __restrict__ q,
-                                                      const uint16_t* __restrict__ k,
-                                                      const uint16_t* __restrict__ v,
-                                                      uint16_t* __restrict__ o,
-                                                      float* __restrict__ lse, int BH, int T,
-                                                      float scale) {
+struct FwdState {
+  f32x16 oacc[HS / 32];
+  float m, l;
+};
+
+// One key tile for one wavefront.  MASK: the tile reaches past this
+// wavefront's first query (keys > query are set to -inf).
+template <int HS, bool MASK>
+__device__ inline void fwd_tile(const uint16_t* Kb, const uint16_t* Vb, int key0, int qrow,
+                                int h, float c, const LaneOffsets<HS>& L,
+                                const u32x4 (&qf)[HS / 16], FwdState<HS>& st) {
   using C = FwdCfg<HS>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[C::BN * C::KST];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[HS * C::VST];
+  f32x16 s[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    s[kh] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEP; ++ks)
+      s[kh] = mfma32(op_nat<HS>(Kb, L, kh * 32, ks), qf[ks], s[kh]);
+  }
+  // Register i of s[kh] is key key0 + kh*32 + 16*(i/8) + 8h + i%8, query qrow.
+  if (MASK) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + kh * 32 + 16 * (i >> 3) + 8 * h + (i & 7) > qrow) s[kh][i] = -INFINITY;
+  }
+  float mt = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int i = (kh == 0 ? 2 : 0); i < 16; i += 2) mt = fmaxf(mt, fmaxf(s[kh][i], s[kh][i + 1]));
+  mt = halves_max(mt);
+  // Each row moves its reference max only if its weights would exceed 2^8
+  // (a per-row decision, so a row's result never depends on other rows).
+  // The multiply is skipped when no row of the wavefront moved; rows that
+  // keep their max are multiplied by exactly 1.
+  const float mn = (mt - st.m) * c > 8.f ? fmaxf(st.m, mt) : st.m;
+  if (__builtin_amdgcn_ballot_w64(mn != st.m)) {
+    const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);  // m = -inf first: alpha = 0
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.oacc[db][i] *= alpha;
+    st.m = mn;
+  }
+  const float mc = st.m * c;
+  u32x4 pf[2][2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e + 1], c, -mc));
+        pf[kh][t][e] = pack_bf16(p0, p1);
+        st.l += p0 + p1;
+      }
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        st.oacc[db] = mfma32(op_tr<HS>(Vb, L, kh * 32 + 16 * t, db), pf[kh][t], st.oacc[db]);
+}
+
+template <int HS>
+__global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v,
+                                                           uint16_t* __restrict__ o,
+                                                           float* __restrict__ lse, int BH, int T,
+                                                           float scale) {
+  using C = FwdCfg<HS>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::BN * HS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::BN * HS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -63,168 +135,84 @@ __global__ __launch_bounds__(256) void bf16_fwd_kernel(const uint16_t* __restric
   const int qt = nqt - 1 - int(blockIdx.x) / BH;
   const int bh = int(blockIdx.x) % BH;
   const long base = long(bh) * T * HS;
-  const uint16_t* qb = q + base;
-  const uint16_t* kb = k + base;
-  const uint16_t* vb = v + base;
+  const uint32_t slice_bytes = uint32_t(T) * HS * 2;
+  const rsrc_t rq = make_rsrc(q + base, slice_bytes), rk = make_rsrc(k + base, slice_bytes);
+  const rsrc_t rv = make_rsrc(v + base, slice_bytes);
 
   const int r0 = qt * C::BM;
   const int q0 = r0 + 32 * w;  // first query row of this wavefront
+  const int qrow = q0 + n;
   const int nkt = (min(r0 + C::BM, T) - 1) / C::BN + 1;
   const float c = scale * kLog2e;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  // Q^T as the MFMA B operand: lane (n, h) holds Q[q0 + n][16 ks + 8h .. +7].
-  const int qrow = q0 + n;
+  auto issue = [&](int kt, int buf) {
+    dma_tile<HS, C::BN, C::NW>(rk, kt * C::BN, Ks[buf], w, lane);
+    dma_tile<HS, C::BN, C::NW>(rv, kt * C::BN, Vs[buf], w, lane);
+  };
+  issue(0, 0);
+
+  // Q^T as the MFMA B operand: lane (n, h) holds Q[qrow][16 ks + 8h .. +7].
   u32x4 qf[C::KSTEP];
 #pragma unroll
   for (int ks = 0; ks < C::KSTEP; ++ks)
-    qf[ks] = qrow < T ? *reinterpret_cast<const u32x4*>(qb + long(qrow) * HS + 16 * ks + 8 * h)
-                      : zero4;
+    qf[ks] = bload16(rq, uint32_t(qrow * HS + 16 * ks + 8 * h) * 2);
 
-  // Register staging of the next K / V tile.
-  u32x4 kr[C::KPT];
-  uint32_t vr[8];
-  auto gload = [&](int kt) {
+  FwdState<HS> st;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) st.oacc[db] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const LaneOffsets<HS> L(lane);
+
+  wait_vmem();
+  __syncthreads();
+  // One tile: prefetch the next into the other buffer, compute, publish.
+  // Unrolled by two so that each buffer's LDS offsets are immediates.
+  auto step = [&](int kt, const uint16_t* Kb, const uint16_t* Vb, int nbuf) {
+    if (kt + 1 < nkt) issue(kt + 1, nbuf);
     const int key0 = kt * C::BN;
-#pragma unroll
-    for (int j = 0; j < C::KPT; ++j) {
-      const int ch = tid + 256 * j, row = ch / (HS / 8), col = ch % (HS / 8);
-      const int key = key0 + row;
-      kr[j] = key < T ? *reinterpret_cast<const u32x4*>(kb + long(key) * HS + col * 8) : zero4;
+    if (q0 < T && key0 <= q0 + 31) {  // this wavefront sees some key of the tile
+      if (key0 + C::BN - 1 > q0)
+        fwd_tile<HS, true>(Kb, Vb, key0, qrow, h, c, L, qf, st);
+      else
+        fwd_tile<HS, false>(Kb, Vb, key0, qrow, h, c, L, qf, st);
     }
-    if (tid < C::VU) {
-      const int dp = tid % (HS / 2), kg = tid / (HS / 2);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int key = key0 + kg * 8 + r;
-        vr[r] = key < T ? *reinterpret_cast<const uint32_t*>(vb + long(key) * HS + 2 * dp) : 0u;
-      }
-    }
+    wait_vmem();
+    __syncthreads();
   };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int j = 0; j < C::KPT; ++j) {
-      const int ch = tid + 256 * j, row = ch / (HS / 8), col = ch % (HS / 8);
-      *reinterpret_cast<u32x4*>(Ks + row * C::KST + col * 8) = kr[j];
-    }
-    if (tid < C::VU) {
-      const int dp = tid % (HS / 2), kg = tid / (HS / 2);
-      u32x4 lo, hi;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        lo[t] = (vr[2 * t] & 0xffffu) | (vr[2 * t + 1] << 16);
-        hi[t] = (vr[2 * t] >> 16) | (vr[2 * t + 1] & 0xffff0000u);
-      }
-      *reinterpret_cast<u32x4*>(Vt + (2 * dp) * C::VST + kg * 8) = lo;
-      *reinterpret_cast<u32x4*>(Vt + (2 * dp + 1) * C::VST + kg * 8) = hi;
-    }
-  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(kt, Ks[0], Vs[0], 1);
+    if (kt + 1 < nkt) step(kt + 1, Ks[1], Vs[1], 0);
+  }
 
-  f32x16 oacc[C::DB];
+  // The first processed tile holds key 0 <= every query, so m is finite and
+  // l > 0 for every real row.  O^T register i of lane (n, h): column
+  // d = db*32 + 8*(i/4) + 4h + i%4 of row qrow.
+  const float lt = halves_sum(st.l);
+  const float inv = 1.f / lt;
+  const rsrc_t wo = make_rsrc(o + base, slice_bytes);
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m = -INFINITY, l = 0.f;
-  const int prow = perm_row(n);
-
-  gload(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (kt + 1 < nkt) gload(kt + 1);
-    const int key0 = kt * C::BN;
-    if (q0 >= T || key0 > q0 + 31) continue;  // wavefront has no visible key here
-
-    f32x16 s[2];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[kh][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C::KSTEP; ++ks) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(Ks + (kh * 32 + prow) * C::KST + 16 * ks + 8 * h);
-        s[kh] = mfma32(a, qf[ks], s[kh]);
-      }
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t off = uint32_t(qrow * HS + db * 32 + 8 * g + 4 * h) * 2;
+      bstore8(wo, off, u32x2{pack_bf16(st.oacc[db][4 * g] * inv, st.oacc[db][4 * g + 1] * inv),
+                             pack_bf16(st.oacc[db][4 * g + 2] * inv, st.oacc[db][4 * g + 3] * inv)});
     }
-    // Causal mask on tiles that reach past this wavefront's first query.
-    if (key0 + C::BN - 1 > q0) {
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + kh * 32 + 16 * (i >> 3) + 8 * h + (i & 7);
-          if (key > qrow) s[kh][i] = -INFINITY;
-        }
-    }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kh][i]);
-    mt = halves_max(mt);
-    const float mn = fmaxf(m, mt);
-    const float alpha = __builtin_amdgcn_exp2f((m - mn) * c);
-    const float mc = mn * c;
-    float ls = 0.f;
-    u32x4 pf[2][2];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e], c, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e + 1], c, -mc));
-          ls += p0 + p1;
-          pf[kh][t][e] = pack_bf16(p0, p1);
-        }
-    l = l * alpha + ls;
-    m = mn;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(Vt + (db * 32 + n) * C::VST + kh * 32 +
-                                                          16 * t + 8 * h);
-          oacc[db] = mfma32(a, pf[kh][t], oacc[db]);
-        }
-  }
-
-  if (q0 >= T) return;
-  const float lt = halves_sum(l);
-  if (qrow < T) {
-    const float inv = 1.f / lt;
-    uint16_t* orow = o + base + long(qrow) * HS;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 val = {pack_bf16(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv),
-                     pack_bf16(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * g + 4 * h) = val;
-      }
-    if (lse != nullptr && h == 0) lse[long(bh) * T + qrow] = m * scale + logf(lt);
-  }
+  if (lse != nullptr && h == 0)
+    bstoref(make_rsrc(lse + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4,
+            st.m * scale + logf(lt));
 }
 
 }  // namespace
 
 hipError_t bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                     float* lse, int BH, int T, int hs, float scale, hipStream_t s) {
-  const int bm = 128;
+  const int bm = FwdCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
   if (hs == 64)
-    return launch(bf16_fwd_kernel<64>, grid, dim3(256), s, q, k, v, o, lse, BH, T, scale);
-  return launch(bf16_fwd_kernel<32>, grid, dim3(256), s, q, k, v, o, lse, BH, T, scale);
+    return launch(bf16_fwd_kernel<64>, grid, dim3(kThreads), s, q, k, v, o, lse, BH, T, scale);
+  return launch(bf16_fwd_kernel<32>, grid, dim3(kThreads), s, q, k, v, o, lse, BH, T, scale);
 }
 
 }  // namespace gattn
