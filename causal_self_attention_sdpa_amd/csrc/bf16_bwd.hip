@@ -249,9 +249,11 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dkdv_kernel(
     if (j < nsteps) issue(qt0 + j, j);
   wait_ring<C::NS, C::PER>(min(C::NS - 2, nsteps - 1));
   __syncthreads();
-  for (int t = 0; t < nsteps; ++t) {
-    const int buf = t % C::NS;
-    if (t + C::NS - 1 < nsteps) issue(qt0 + t + C::NS - 1, (t + C::NS - 1) % C::NS);
+  // One step: prefetch step t+NS-1 into the buffer freed by step t-1, compute
+  // step t, wait until step t+1 has landed, publish.
+  auto step = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    if (t + C::NS - 1 < nsteps) issue(qt0 + t + C::NS - 1, (buf + C::NS - 1) % C::NS);
     const int qs0 = (qt0 + t) * C::BQ;
     if (qs0 < k0 + C::BN)
       dkdv_step_diag<HS>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, kw0, krow, h, c, L, R);
@@ -259,7 +261,8 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dkdv_kernel(
       dkdv_step_full<HS>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, krow, h, c, L, R);
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nsteps - t - 2)));
     __syncthreads();
-  }
+  };
+  ring_loop<C::NS>(nsteps, step);
 
   // dK^T / dV^T register i of lane (n, h): column d = db*32 + 8*(i/4) + 4h + i%4, key krow.
   const rsrc_t wk = make_rsrc(dk + base, slice_bytes), wv = make_rsrc(dv + base, slice_bytes);
@@ -407,11 +410,13 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dq_kernel(
   for (int db = 0; db < C::DB; ++db) dqa[db] = f32x16{};
 
   const LaneOffsets<HS> L(lane);
-  wait_vmem();  // the first stages and this wavefront's q, dO, O, lse rows
+  wait_vmem();  // the first tile and this wavefront's q, dO, O, lse rows
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt % C::NS;
-    if (kt + C::NS - 1 < nkt) issue(kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
+  // One step: prefetch key tile kt+NS-1 into the buffer freed by tile kt-1,
+  // compute tile kt, wait until tile kt+1 has landed, publish.
+  auto step = [&](int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    if (kt + C::NS - 1 < nkt) issue(kt + C::NS - 1, (buf + C::NS - 1) % C::NS);
     const int key0 = kt * C::BN;
     if (q0 < T && key0 <= q0 + 31) {
       if (key0 + C::BN - 1 > q0)
@@ -421,7 +426,8 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dq_kernel(
     }
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
-  }
+  };
+  ring_loop<C::NS>(nkt, step);
 
   // dQ^T register i of lane (n, h): column d = db*32 + 8*(i/4) + 4h + i%4, query qrow.
   const rsrc_t wq = make_rsrc(dq + base, slice_bytes);

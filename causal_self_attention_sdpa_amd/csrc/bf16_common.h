@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace gattn {
 
@@ -195,6 +196,23 @@ __device__ inline void wait_vmem_n() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 __device__ inline void wait_vmem() { wait_vmem_n<0>(); }
+
+// Runs step(t, std::integral_constant<int, t % NS>) for t = t0 .. min(t0+NS, n)-1,
+// so that inside a step the ring buffer index is a compile-time constant
+// (its LDS offsets become instruction immediates).
+template <int B, int NS, class F>
+__device__ inline void ring_block(int t0, int n, F& step) {
+  if constexpr (B < NS) {
+    if (t0 + B < n) {
+      step(t0 + B, std::integral_constant<int, B>{});
+      ring_block<B + 1, NS>(t0, n, step);
+    }
+  }
+}
+template <int NS, class F>
+__device__ inline void ring_loop(int n, F& step) {
+  for (int t0 = 0; t0 < n; t0 += NS) ring_block<0, NS>(t0, n, step);
+}
 
 // Ring of NS LDS stages fed by DMA: before computing step t, step t+NS-1 is
 // issued; after it, the caller needs step t+1 complete, i.e. at most the DMA

@@ -31,6 +31,10 @@
 #include "bf16_common.h"
 #include "gattn_internal.h"
 
+#ifndef GATTN_FWD_STAGES
+#define GATTN_FWD_STAGES 2
+#endif
+
 namespace gattn {
 namespace {
 
@@ -43,6 +47,8 @@ struct FwdCfg {
   static constexpr int BN = 64;           // key rows per tile
   static constexpr int KSTEP = HS / 16;   // MFMA k-steps over hs
   static constexpr int DB = HS / 32;      // 32-wide blocks of hs
+  static constexpr int NS = GATTN_FWD_STAGES;            // LDS ring depth
+  static constexpr int PER = 2 * (BN * HS / 512) / NW;  // DMA instructions per wavefront per tile
   static_assert((BN * HS / 512) % NW == 0, "uniform DMA split");
 };
 
@@ -125,8 +131,8 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
                                                            float* __restrict__ lse, int BH, int T,
                                                            float scale) {
   using C = FwdCfg<HS>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::BN * HS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::BN * HS];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[C::NS][C::BN * HS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[C::NS][C::BN * HS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -149,7 +155,9 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
     dma_tile<HS, C::BN, C::NW>(rk, kt * C::BN, Ks[buf], w, lane);
     dma_tile<HS, C::BN, C::NW>(rv, kt * C::BN, Vs[buf], w, lane);
   };
-  issue(0, 0);
+#pragma unroll
+  for (int j = 0; j < C::NS - 1; ++j)
+    if (j < nkt) issue(j, j);
 
   // Q^T as the MFMA B operand: lane (n, h) holds Q[qrow][16 ks + 8h .. +7].
   u32x4 qf[C::KSTEP];
@@ -166,24 +174,22 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
 
   wait_vmem();
   __syncthreads();
-  // One tile: prefetch the next into the other buffer, compute, publish.
-  // Unrolled by two so that each buffer's LDS offsets are immediates.
-  auto step = [&](int kt, const uint16_t* Kb, const uint16_t* Vb, int nbuf) {
-    if (kt + 1 < nkt) issue(kt + 1, nbuf);
+  // One tile: prefetch tile kt+NS-1 into the buffer freed by tile kt-1,
+  // compute tile kt, wait until tile kt+1 has landed, publish.
+  auto step = [&](int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    if (kt + C::NS - 1 < nkt) issue(kt + C::NS - 1, (buf + C::NS - 1) % C::NS);
     const int key0 = kt * C::BN;
     if (q0 < T && key0 <= q0 + 31) {  // this wavefront sees some key of the tile
       if (key0 + C::BN - 1 > q0)
-        fwd_tile<HS, true>(Kb, Vb, key0, qrow, h, c, L, qf, st);
+        fwd_tile<HS, true>(Ks[buf], Vs[buf], key0, qrow, h, c, L, qf, st);
       else
-        fwd_tile<HS, false>(Kb, Vb, key0, qrow, h, c, L, qf, st);
+        fwd_tile<HS, false>(Ks[buf], Vs[buf], key0, qrow, h, c, L, qf, st);
     }
-    wait_vmem();
+    wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
   };
-  for (int kt = 0; kt < nkt; kt += 2) {
-    step(kt, Ks[0], Vs[0], 1);
-    if (kt + 1 < nkt) step(kt + 1, Ks[1], Vs[1], 0);
-  }
+  ring_loop<C::NS>(nkt, step);
 
   // The first processed tile holds key 0 <= every query, so m is finite and
   // l > 0 for every real row.  O^T register i of lane (n, h): column
