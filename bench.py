@@ -14,6 +14,9 @@ causal pairs j <= i, P_c = T (T + 1) / 2 per (b, h)):
 Prints one JSON line.  `roofline` is for the dominant kernel (the one with the
 largest mean duration): its algorithmic FLOP per launch / that mean duration,
 measured with HIP events recorded on the launch stream inside the timed steps.
+Each timed step brackets the three kernels of one layer with events (layer
+s mod L in step s, so every layer is sampled); bracketing every launch would
+itself cost about a tenth of the step time.
 Algorithmic FLOP per causal pair and kernel: forward 4 hs (Q K^T and P V);
 dK/dV kernel 6 hs (dO V^T, P^T dO, dS^T Q; its Q K^T is recomputation); dQ
 kernel 2 hs (dS K; its Q K^T and dO V^T are recomputation).
@@ -147,9 +150,8 @@ def main() -> int:
     ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream()
-    nb = args.steps * L
     ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(nb)] for k in KERNELS}
+              for _ in range(args.steps)] for k in KERNELS}
 
     # C-ABI argument tuples, marshalled once: the timed loop is nothing but
     # library calls (and event records), so the host keeps ahead of the GPU.
@@ -181,10 +183,12 @@ def main() -> int:
             raise RuntimeError(f"{name} failed with status {st}")
 
     def step(record: int | None):
+        # record = index of a timed step: its events bracket the kernels of layer record % L
+        lt = None if record is None else record % L
         for l in range(L):
-            run(l, "fwd", None if record is None else record * L + l)
+            run(l, "fwd", record if l == lt else None)
         for l in reversed(range(L)):
-            i = None if record is None else record * L + l
+            i = record if l == lt else None
             run(l, "dq", i)
             run(l, "dkdv", i)
 

@@ -9,7 +9,9 @@
 // Work split: one workgroup = 4 wavefronts = 128 query rows of one (b, h);
 // wavefront w owns rows r0 + 32w .. r0 + 32w + 31.  64-row key and value
 // tiles arrive in double-buffered, swizzled LDS tiles by LDS DMA; tiles
-// entirely above the diagonal are never loaded.  Per tile and wavefront:
+// entirely above the diagonal are never loaded, and of the tile on a
+// wavefront's diagonal only the 32x32 blocks not entirely above it are
+// computed (the mask touches one block).  Per tile and wavefront:
 //   S^T (keys x queries) = K Q^T   on MFMA, Q^T held in registers for the
 //                                   whole loop (B operand), K rows read from
 //                                   LDS in perm_row order so each lane's
@@ -58,35 +60,48 @@ struct FwdState {
   float m, l;
 };
 
-// One key tile for one wavefront.  MASK: the tile reaches past this
-// wavefront's first query (keys > query are set to -inf).
-template <int HS, bool MASK>
-__device__ inline void fwd_tile(const uint16_t* Kb, const uint16_t* Vb, int key0, int qrow,
-                                int h, float c, const LaneOffsets<HS>& L,
-                                const u32x4 (&qf)[HS / 16], FwdState<HS>& st) {
+// Kinds of key tile for one wavefront (32 queries q0 .. q0+31, 64 keys from
+// key0, q0 - key0 a multiple of 32):
+//   kFull  : every key <= every query;
+//   kDiagLo: key0 == q0, so keys key0 .. key0+31 form the 32x32 diagonal
+//            block and keys key0+32 .. key0+63 lie above every query (skipped);
+//   kDiagHi: key0 + 32 == q0: the first 32 keys are full, the second 32 form
+//            the diagonal block.
+enum TileKind { kFull = 0, kDiagLo = 1, kDiagHi = 2 };
+
+// One key tile for one wavefront.  `dn` = n - 8h: in the diagonal block,
+// register i of lane (n, h) holds key (q0 + 16*(i/8) + 8h + i%8), which lies
+// above query q0 + n exactly when 16*(i/8) + i%8 > dn.
+template <int HS, int KIND>
+__device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb, int dn, float c,
+                                         const LaneOffsets<HS>& L, const u32x4 (&qf)[HS / 16],
+                                         FwdState<HS>& st) {
   using C = FwdCfg<HS>;
+  constexpr int NKH = KIND == kDiagLo ? 1 : 2;  // 32-key halves computed
   f32x16 s[2];
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
+  for (int kh = 0; kh < NKH; ++kh) {
     s[kh] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEP; ++ks)
       s[kh] = mfma32(op_nat<HS>(Kb, L, kh * 32, ks), qf[ks], s[kh]);
   }
-  // Register i of s[kh] is key key0 + kh*32 + 16*(i/8) + 8h + i%8, query qrow.
-  if (MASK) {
+  // Register i of s[kh] is key key0 + kh*32 + 16*(i/8) + 8h + i%8, query q0 + n.
+  if (KIND != kFull) {
+    constexpr int kd = KIND == kDiagLo ? 0 : 1;  // the diagonal half
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (key0 + kh * 32 + 16 * (i >> 3) + 8 * h + (i & 7) > qrow) s[kh][i] = -INFINITY;
+    for (int i = 0; i < 16; ++i)
+      if (16 * (i >> 3) + (i & 7) > dn) s[kd][i] = -INFINITY;
   }
-  float mt = fmaxf(s[0][0], s[0][1]);
+  // Row max: one max3 chain per half.
+  float mh[NKH];
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
+  for (int kh = 0; kh < NKH; ++kh) {
+    mh[kh] = fmaxf(s[kh][0], s[kh][1]);
 #pragma unroll
-    for (int i = (kh == 0 ? 2 : 0); i < 16; i += 2) mt = fmaxf(mt, fmaxf(s[kh][i], s[kh][i + 1]));
-  mt = halves_max(mt);
+    for (int i = 2; i < 16; i += 2) mh[kh] = fmaxf(fmaxf(mh[kh], s[kh][i]), s[kh][i + 1]);
+  }
+  const float mt = halves_max(NKH == 2 ? fmaxf(mh[0], mh[1]) : mh[0]);
   // Each row moves its reference max only if its weights would exceed 2^8
   // (a per-row decision, so a row's result never depends on other rows).
   // The multiply is skipped when no row of the wavefront moved; rows that
@@ -96,15 +111,13 @@ __device__ inline void fwd_tile(const uint16_t* Kb, const uint16_t* Vb, int key0
     const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);  // m = -inf first: alpha = 0
     st.l *= alpha;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.oacc[db][i] *= alpha;
+    for (int db = 0; db < C::DB; ++db) st.oacc[db] *= alpha;
     st.m = mn;
   }
   const float mc = st.m * c;
   u32x4 pf[2][2];
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
+  for (int kh = 0; kh < NKH; ++kh)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -115,7 +128,7 @@ __device__ inline void fwd_tile(const uint16_t* Kb, const uint16_t* Vb, int key0
         st.l += p0 + p1;
       }
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
+  for (int kh = 0; kh < NKH; ++kh)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -170,6 +183,7 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
   for (int db = 0; db < C::DB; ++db) st.oacc[db] = f32x16{};
   st.m = -INFINITY;
   st.l = 0.f;
+  const int dn = n - 8 * h;
   const LaneOffsets<HS> L(lane);
 
   wait_vmem();
@@ -180,11 +194,13 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
     constexpr int buf = decltype(bufc)::value;
     if (kt + C::NS - 1 < nkt) issue(kt + C::NS - 1, (buf + C::NS - 1) % C::NS);
     const int key0 = kt * C::BN;
-    if (q0 < T && key0 <= q0 + 31) {  // this wavefront sees some key of the tile
-      if (key0 + C::BN - 1 > q0)
-        fwd_tile<HS, true>(Ks[buf], Vs[buf], key0, qrow, h, c, L, qf, st);
+    if (q0 < T && key0 <= q0) {  // this wavefront sees some key of the tile
+      if (key0 == q0)
+        fwd_tile<HS, kDiagLo>(Ks[buf], Vs[buf], dn, c, L, qf, st);
+      else if (key0 + 32 == q0)
+        fwd_tile<HS, kDiagHi>(Ks[buf], Vs[buf], dn, c, L, qf, st);
       else
-        fwd_tile<HS, false>(Ks[buf], Vs[buf], key0, qrow, h, c, L, qf, st);
+        fwd_tile<HS, kFull>(Ks[buf], Vs[buf], dn, c, L, qf, st);
     }
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
