@@ -34,6 +34,12 @@
 #ifndef GATTN_DQ_STAGES
 #define GATTN_DQ_STAGES 2
 #endif
+#ifndef GATTN_DKDV_OCC
+#define GATTN_DKDV_OCC 2
+#endif
+#ifndef GATTN_DQ_OCC
+#define GATTN_DQ_OCC 2
+#endif
 
 namespace gattn {
 namespace {
@@ -82,9 +88,8 @@ __global__ __launch_bounds__(kThreads) void bf16_pre_kernel(const uint16_t* __re
 //   B(b): P, dS (f32, registers) -> bf16, exactly the B operand of
 //   C(b): dV^T += dO^T P, dK^T += Q^T dS   C[d][key]; dO^T, Q^T via LDS
 //                                          transpose reads
-// Below the diagonal the blocks are software-pipelined: A(b+1) is issued
-// before B(b), so the matrix cores work on the next block while the vector
-// ALUs do this one's softmax terms.
+// In the steps that meet the diagonal, blocks wholly before this wavefront's
+// keys are skipped and the others masked.
 template <int HS>
 struct DkdvCfg {
   static constexpr int NW = 4;
@@ -162,7 +167,7 @@ __device__ inline void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const f
     }
 }
 
-// One step below the diagonal: every block is visible, no mask, pipelined.
+// One step below the diagonal: every block is visible, no mask.
 template <int HS>
 __device__ inline void dkdv_step_full(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
                                       const float* Db, int qs0, int krow, int h, float c,
@@ -193,7 +198,7 @@ __device__ inline void dkdv_step_diag(const uint16_t* Qb, const uint16_t* Gb, co
 }
 
 template <int HS>
-__global__ __launch_bounds__(kThreads, 2) void bf16_dkdv_kernel(
+__global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void bf16_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
     const float* __restrict__ Dg, const float* __restrict__ L2g, uint16_t* __restrict__ dk,
@@ -302,15 +307,26 @@ struct DqCfg {
   static_assert((BN * HS / 512) % NW == 0, "uniform DMA split");
 };
 
-template <int HS, bool MASK>
-__device__ inline void dq_step(const uint16_t* Kb, const uint16_t* Vb, int key0, int qrow, int h,
-                               float c, float lse2, float Dq, const LaneOffsets<HS>& L,
-                               const u32x4 (&qf)[HS / 16], const u32x4 (&gf)[HS / 16],
-                               f32x16 (&dqa)[HS / 32]) {
+// Kinds of key tile for one wavefront (32 queries q0 .. q0+31, 64 keys from
+// key0, q0 - key0 a multiple of 32): kFull, every key <= every query;
+// kDiagLo, key0 == q0: the first 32 keys form the diagonal block, the other
+// 32 lie after every query (skipped); kDiagHi, key0 + 32 == q0: the second
+// 32 keys form the diagonal block.  In the diagonal block register 8t+e of
+// lane (n, h) holds key (q0 + 16t + 8h + e), after query q0 + n exactly when
+// 16t + e > dn = n - 8h.
+enum DqTile { kFull = 0, kDiagLo = 1, kDiagHi = 2 };
+
+template <int HS, int KIND>
+__device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, int dn, float c,
+                                        float lse2, float Dq, const LaneOffsets<HS>& L,
+                                        const u32x4 (&qf)[HS / 16], const u32x4 (&gf)[HS / 16],
+                                        f32x16 (&dqa)[HS / 32]) {
   using C = DqCfg<HS>;
+  constexpr int NKB = KIND == kDiagLo ? 1 : 2;  // 32-key blocks computed
+  constexpr int KD = KIND == kDiagLo ? 0 : (KIND == kDiagHi ? 1 : -1);  // the diagonal block
   u32x4 dsp[2][2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < NKB; ++kb) {
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEP; ++ks) {
@@ -323,7 +339,7 @@ __device__ inline void dq_step(const uint16_t* Kb, const uint16_t* Vb, int key0,
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float p = __builtin_amdgcn_exp2f(fmaf(st[8 * t + e], c, -lse2));
-        if (MASK && key0 + kb * 32 + 16 * t + 8 * h + e > qrow) p = 0.f;
+        if (kb == KD && 16 * t + e > dn) p = 0.f;
         dsv[e] = p * (dpt[8 * t + e] - Dq);
       }
 #pragma unroll
@@ -331,7 +347,7 @@ __device__ inline void dq_step(const uint16_t* Kb, const uint16_t* Vb, int key0,
     }
   }
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -340,7 +356,7 @@ __device__ inline void dq_step(const uint16_t* Kb, const uint16_t* Vb, int key0,
   // Scheduling hint: spread the MFMAs over the step, each followed by vector
   // ALU work and LDS reads of other blocks, instead of phase after phase.
 #pragma unroll
-  for (int i = 0; i < 8 * C::KSTEP + 4 * C::DB; ++i) {
+  for (int i = 0; i < NKB * (2 * C::KSTEP + 2 * C::DB); ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -348,7 +364,7 @@ __device__ inline void dq_step(const uint16_t* Kb, const uint16_t* Vb, int key0,
 }
 
 template <int HS>
-__global__ __launch_bounds__(kThreads, 2) void bf16_dq_kernel(
+__global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, float* __restrict__ Dg,
@@ -371,6 +387,7 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dq_kernel(
   const int r0 = qt * C::BM;
   const int q0 = r0 + 32 * w;
   const int qrow = q0 + n;
+  const int dn = n - 8 * h;
   const float c = scale * kLog2e;
 
   auto issue = [&](int kt, int buf) {
@@ -418,11 +435,13 @@ __global__ __launch_bounds__(kThreads, 2) void bf16_dq_kernel(
     constexpr int buf = decltype(bufc)::value;
     if (kt + C::NS - 1 < nkt) issue(kt + C::NS - 1, (buf + C::NS - 1) % C::NS);
     const int key0 = kt * C::BN;
-    if (q0 < T && key0 <= q0 + 31) {
-      if (key0 + C::BN - 1 > q0)
-        dq_step<HS, true>(Ks[buf], Vs[buf], key0, qrow, h, c, lse2, Dq, L, qf, gf, dqa);
+    if (q0 < T && key0 <= q0) {
+      if (key0 == q0)
+        dq_step<HS, kDiagLo>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
+      else if (key0 + 32 == q0)
+        dq_step<HS, kDiagHi>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
       else
-        dq_step<HS, false>(Ks[buf], Vs[buf], key0, qrow, h, c, lse2, Dq, L, qf, gf, dqa);
+        dq_step<HS, kFull>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
     }
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
