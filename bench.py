@@ -16,7 +16,9 @@ largest mean duration): its algorithmic FLOP per launch / that mean duration,
 measured with HIP events recorded on the launch stream inside the timed steps.
 Each timed step brackets the three kernels of one layer with events (layer
 s mod L in step s, so every layer is sampled); bracketing every launch would
-itself cost about a tenth of the step time.
+itself cost about a tenth of the step time.  The events are created with
+hipEventDisableSystemFence: timing only, without the cache writeback and
+invalidation of a default event, which would slow the kernels they bracket.
 Algorithmic FLOP per causal pair and kernel: forward 4 hs (Q K^T and P V);
 dK/dV kernel 6 hs (dO V^T, P^T dO, dS^T Q; its Q K^T is recomputation); dQ
 kernel 2 hs (dS K; its Q K^T and dO V^T are recomputation).
@@ -74,25 +76,67 @@ def read_traffic(name: str):
     return float(t.group(1))
 
 
-def cpu_baseline(x, scale, nslices: int):
-    """The CPU oracle (as it stands) on the first `nslices` (b, h) slices of
-    layer 0, all host threads of this process's CPU share (at most 16)."""
+def cpu_baseline(host_layers, scale, nslices: int):
+    """The CPU oracle (as it stands) on the first `nslices` (layer, b, h)
+    slices of the workload, all host threads of this process's CPU share (at
+    most 16)."""
     import numpy as np
 
     import oracle
 
-    B, H, T, hs = x["q"].shape
-    idx = [(b, h) for b in range(B) for h in range(H)][:nslices]
-    sel = {n: np.stack([a[b, h] for b, h in idx])[:, None] for n, a in x.items()}
+    B, H, T, hs = host_layers[0]["q"].shape
+    idx = [(l, b, h) for l in range(len(host_layers)) for b in range(B) for h in range(H)]
+    idx = idx[:nslices]
+    sel = {n: np.stack([host_layers[l][n][b, h] for l, b, h in idx])[:, None]
+           for n in ("q", "k", "v", "do")}
     threads = min(16, len(os.sched_getaffinity(0)))
     t0 = time.perf_counter()
     oracle.attention_backward(sel["q"], sel["k"], sel["v"], sel["do"], scale, nthreads=threads)
     dt = time.perf_counter() - t0
     ff, fb = flops(len(idx), 1, T, hs)
+    nl = idx[-1][0] + 1
     return {"value": round((ff + fb) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{len(idx)} of {B * H} (b,h) slices of layer 0 (T={T}, hs={hs}), "
-                      f"forward+backward in float64, FLOP counted as on the GPU"}
+            "sample": f"{len(idx)} of the {B * H * len(host_layers)} (layer,b,h) slices "
+                      f"(layers 0..{nl - 1}; T={T}, hs={hs}), forward+backward in float64, "
+                      f"FLOP counted as on the GPU"}
+
+
+class HipTimer:
+    """Timing events of the HIP runtime torch has loaded, created with
+    hipEventDisableSystemFence (recording one does not write back and
+    invalidate the caches)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = self.ct.c_void_p()
+        st = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+        return e
+
+    def record(self, e, stream_ptr: int):
+        st = self.hip.hipEventRecord(e, stream_ptr)
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.ct.c_float()
+        st = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
 
 
 def main() -> int:
@@ -100,8 +144,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-slices", type=int, default=48,
-                    help="(b,h) slices the CPU oracle baseline runs (0 to skip)")
+    ap.add_argument("--cpu-slices", type=int, default=400,
+                    help="(layer,b,h) slices the CPU oracle baseline runs (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -135,12 +179,12 @@ def main() -> int:
     print(f"[bench] generating {L} layers of seeded inputs {B}x{H}x{T}x{hs}", file=sys.stderr,
           flush=True)
     layers = []
-    host0 = None
+    host = []  # host copies of the layers the CPU baseline samples
     for l in range(L):
         x = si.attention_inputs(B, H, T, hs, "bf16", seed=2024, workload="gpt2-124m-attn", layer=l,
                                 qkv_scale=W["qkv_scale"])
-        if l == 0:
-            host0 = x
+        if l * B * H < args.cpu_slices:
+            host.append(x)
         t = {n: torch.from_numpy(a).to(dev).to(torch.bfloat16) for n, a in x.items()}
         t["o"] = torch.empty_like(t["q"])
         t["lse"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
@@ -150,8 +194,8 @@ def main() -> int:
     ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream()
-    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for k in KERNELS}
+    timer = HipTimer()
+    ev = {k: [(timer.event(), timer.event()) for _ in range(args.steps)] for k in KERNELS}
 
     # C-ABI argument tuples, marshalled once: the timed loop is nothing but
     # library calls (and event records), so the host keeps ahead of the GPU.
@@ -175,10 +219,10 @@ def main() -> int:
     def run(l, name, idx):
         fn, a = call[l][name]
         if idx is not None and name in ev:
-            ev[name][idx][0].record(stream)
+            timer.record(ev[name][idx][0], sp)
         st = fn(*a)
         if idx is not None and name in ev:
-            ev[name][idx][1].record(stream)
+            timer.record(ev[name][idx][1], sp)
         if st != 0:
             raise RuntimeError(f"{name} failed with status {st}")
 
@@ -207,7 +251,8 @@ def main() -> int:
     ms_per_step = dt / args.steps * 1e3
     value = step_flops * args.steps / dt / 1e12
     pairs = B * H * T * (T + 1) // 2
-    mean_us = {k: float(np.mean([a.elapsed_time(b) for a, b in ev[k]])) * 1e3 for k in KERNELS}
+    mean_us = {k: float(np.mean([timer.elapsed_ms(a, b) for a, b in ev[k]])) * 1e3
+               for k in KERNELS}
     dom = max(mean_us, key=mean_us.get)
     alg = KERNELS[dom][2] * hs * pairs
     achieved = alg / (mean_us[dom] * 1e-6) / 1e12
@@ -240,7 +285,7 @@ def main() -> int:
     if args.cpu_slices > 0:
         print(f"[bench] timing the CPU oracle on {args.cpu_slices} slices", file=sys.stderr,
               flush=True)
-        out["cpu_baseline"] = cpu_baseline(host0, scale, args.cpu_slices)
+        out["cpu_baseline"] = cpu_baseline(host, scale, args.cpu_slices)
     print(json.dumps(out), flush=True)
     return 0
 
