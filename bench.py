@@ -23,6 +23,13 @@ Algorithmic FLOP per causal pair and kernel: forward 4 hs (Q K^T and P V);
 dK/dV kernel 6 hs (dO V^T, P^T dO, dS^T Q; its Q K^T is recomputation); dQ
 kernel 2 hs (dS K; its Q K^T and dO V^T are recomputation).
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+Also reported: the forward and backward sequences of a step (events around
+the L forward launches and around the L backward pairs: median and minimum
+over the timed steps); the throughput under the FlashAttention-style count,
+which charges the backward 10 hs per pair (its recomputation of S); and, after
+the timed steps, a measured dense bf16 matrix-multiply rate (torch.matmul,
+i.e. the vendor GEMM library, on 8192^3) and a measured device-copy bandwidth
+at the run's clocks, next to the published peaks.
 """
 from __future__ import annotations
 
@@ -51,9 +58,39 @@ KERNELS = {  # name -> (kernel symbol, source file, algorithmic FLOP per causal 
 }
 
 
-def flops(B, H, T, hs):
+def flops(B, H, T, hs, bwd_per_pair=8):
     pc = T * (T + 1) // 2
-    return 4 * hs * pc * B * H, 8 * hs * pc * B * H
+    return 4 * hs * pc * B * H, bwd_per_pair * hs * pc * B * H
+
+
+def measured_peaks(torch, dev):
+    """Dense bf16 GEMM rate (torch.matmul, 8192^3) and device-copy bandwidth
+    (1 GiB read + 1 GiB written) at this run's clocks."""
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    reps = 20
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    gemm = 2.0 * n ** 3 * reps / (time.perf_counter() - t0) / 1e12
+    del a, b
+    x = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    copy = 2.0 * x.numel() * 4 * reps / (time.perf_counter() - t0) / 1e9
+    return {"bf16_gemm_tflops": round(gemm, 1), "copy_gbs": round(copy, 1),
+            "gemm": "torch.matmul bf16 8192x8192x8192", "copy": "1 GiB device-to-device"}
 
 
 def source_digest(path: str) -> str:
@@ -146,6 +183,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-slices", type=int, default=400,
                     help="(layer,b,h) slices the CPU oracle baseline runs (0 to skip)")
+    ap.add_argument("--no-peaks", dest="peaks", action="store_false",
+                    help="skip the measured GEMM / copy peaks after the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
@@ -196,6 +235,7 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     timer = HipTimer()
     ev = {k: [(timer.event(), timer.event()) for _ in range(args.steps)] for k in KERNELS}
+    seq = [(timer.event(), timer.event(), timer.event()) for _ in range(args.steps)]
 
     # C-ABI argument tuples, marshalled once: the timed loop is nothing but
     # library calls (and event records), so the host keeps ahead of the GPU.
@@ -229,12 +269,18 @@ def main() -> int:
     def step(record: int | None):
         # record = index of a timed step: its events bracket the kernels of layer record % L
         lt = None if record is None else record % L
+        if record is not None:
+            timer.record(seq[record][0], sp)
         for l in range(L):
             run(l, "fwd", record if l == lt else None)
+        if record is not None:
+            timer.record(seq[record][1], sp)
         for l in reversed(range(L)):
             i = record if l == lt else None
             run(l, "dq", i)
             run(l, "dkdv", i)
+        if record is not None:
+            timer.record(seq[record][2], sp)
 
     for _ in range(args.warmup):
         step(None)
@@ -250,6 +296,10 @@ def main() -> int:
     step_flops = L * (ff + fb)
     ms_per_step = dt / args.steps * 1e3
     value = step_flops * args.steps / dt / 1e12
+    _, fb_fa = flops(B, H, T, hs, bwd_per_pair=10)
+    value_fa = L * (ff + fb_fa) * args.steps / dt / 1e12
+    fwd_ms = [timer.elapsed_ms(a, b) for a, b, _ in seq]
+    bwd_ms = [timer.elapsed_ms(b, c) for _, b, c in seq]
     pairs = B * H * T * (T + 1) // 2
     mean_us = {k: float(np.mean([timer.elapsed_ms(a, b) for a, b in ev[k]])) * 1e3
                for k in KERNELS}
@@ -275,6 +325,9 @@ def main() -> int:
                    "B": B, "H": H, "T": T, "hs": hs, "layers": L, "qkv_scale": W["qkv_scale"],
                    "flop_count": "causal pairs, fwd 4*hs, bwd 8*hs per pair",
                    "parallelism": "single GPU"},
+        "value_flashattention_count": round(value_fa, 3),
+        "fwd_ms": {"median": round(float(np.median(fwd_ms)), 4), "min": round(min(fwd_ms), 4)},
+        "bwd_ms": {"median": round(float(np.median(bwd_ms)), 4), "min": round(min(bwd_ms), 4)},
         "kernels_us": {k: round(v, 2) for k, v in mean_us.items()},
         "roofline": {"kernel": KERNELS[dom][0], "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -282,6 +335,8 @@ def main() -> int:
                      "traffic": read_traffic(dom),
                      "algorithmic_flop_per_launch": alg},
     }
+    if args.peaks:
+        out["measured_peaks"] = measured_peaks(torch, dev)
     if args.cpu_slices > 0:
         print(f"[bench] timing the CPU oracle on {args.cpu_slices} slices", file=sys.stderr,
               flush=True)

@@ -141,3 +141,42 @@ def test_bf16_unit_variance_within_rounding_bound():
     got = pick(gpu_fwd_bwd(x, "bf16", s), sl)
     ref = oracle_slices(x, s, sl)
     check_bound(got, ref, rounding_bound(x, s, sl, ref), where="bf16 hs32 T300")
+
+
+# ------------------------------------------------- every layer of each workload
+# Each layer of a workload draws its own seeded inputs; the workloads repeat the
+# per-layer call over 6 (char-level), 12 (narrow heads, GPT-2 124M) and 48
+# (GPT-2 XL size) layers.  Every layer is checked, on sampled slices at full
+# size; the 48-layer shape is checked on its first, middle and last layers.
+def _layer_slices(B, H, layer, n=2):
+    rng = np.random.default_rng(1000 + layer)
+    return [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("layer", range(6))
+def test_bf16_char_level_every_layer(layer):
+    _sampled(64, 6, 256, 64, 1.0, _layer_slices(64, 6, layer), 1, layer=layer)
+
+
+@pytest.mark.parametrize("T", [128, 256])
+def test_bf16_narrow_heads_every_layer(T):
+    """B=8, H=12, hs=32: all 12 layers, every element of every slice."""
+    import oracle
+    B, H, hs = 8, 12, 32
+    s = default_scale(hs)
+    for layer in range(12):
+        x = inputs(B, H, T, hs, "bf16", seed=33, layer=layer, workload=f"b{B}h{H}t{T}d{hs}")
+        print(f"case bf16 B={B} H={H} T={T} hs={hs} layer={layer}", flush=True)
+        got = gpu_fwd_bwd(x, "bf16", s)
+        ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], s)
+        check_close(got, ref, BF16_TOL, BF16_REL, where=f"bf16 {(B, H, T, hs)} layer {layer}")
+
+
+@pytest.mark.parametrize("layer", range(12))
+def test_bf16_gpt2_small_every_layer(layer):
+    _sampled(12, 12, 1024, 64, 0.5, _layer_slices(12, 12, layer), 2, layer=layer)
+
+
+@pytest.mark.parametrize("layer", [0, 23, 47])
+def test_bf16_gpt2_xl_first_middle_last_layer(layer):
+    _sampled(12, 25, 1024, 64, 1.0, _layer_slices(12, 25, layer), 3, layer=layer)
