@@ -67,9 +67,9 @@ CSRC = os.path.join(ROOT, "causal_self_attention_sdpa_amd", "csrc")
 #          algorithmic bytes per launch in units of one (B,H,T,hs) bf16 tensor, and of one
 #          (B,H,T) fp32 row vector)
 KERNELS = {
-    "fwd": ("bf16_fwd_kernel<{hs}>", "bf16_fwd.hip", 4, 4, 1),   # q k v in, o out; lse out
-    "dq": ("bf16_dq_kernel<{hs}>", "bf16_bwd.hip", 2, 6, 1),     # q k v o dO in, dq out; lse in
-    "dkdv": ("bf16_dkdv_kernel<{hs}>", "bf16_bwd.hip", 6, 6, 0),  # q k v dO in, dk dv out
+    "fwd": ("bf16_fwd_kernel<{hs}, false>", "bf16_fwd.hip", 4, 4, 1),   # q k v in, o, lse out
+    "dq": ("bf16_dq_kernel<{hs}, false>", "bf16_bwd.hip", 2, 6, 1),  # q k v o dO lse in, dq out
+    "dkdv": ("bf16_dkdv_kernel<{hs}, false>", "bf16_bwd.hip", 6, 6, 0),  # q k v dO in, dk dv out
 }
 
 

@@ -8,20 +8,27 @@ or fails to load, importing the binding raises.
 
 Low-level names mirror the C ABI (`gattn_fwd`, `gattn_bwd`, ...) and take
 preallocated torch tensors.  `attention_forward` / `attention_backward`
-allocate the outputs with torch and call those.
+allocate the outputs with torch and call those; `attention_forward_qkv` /
+`attention_backward_qkv` do the same for a GPT block's fused (B, T, 3C)
+projection output, reading q, k, v in place and writing y (B, T, C) and the
+gradient dqkv (B, T, 3C) through the strided entry points.
 """
 from ._binding import (  # noqa: F401
     BF16,
     F32,
     GattnError,
     attention_backward,
+    attention_backward_qkv,
     attention_forward,
+    attention_forward_qkv,
     gattn_bwd,
     gattn_bwd_dkdv,
     gattn_bwd_dq,
     gattn_bwd_preprocess,
+    gattn_bwd_strided,
     gattn_bwd_workspace_bytes,
     gattn_fwd,
+    gattn_fwd_strided,
     gattn_status_string,
     library_path,
     load_library,

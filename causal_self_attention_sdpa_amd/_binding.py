@@ -48,6 +48,10 @@ def load_library():
     lib.gattn_bwd_dq.restype = i
     lib.gattn_bwd_dkdv.argtypes = [vp] * 6 + [i, i, i, i, f, i, vp, sz, vp]
     lib.gattn_bwd_dkdv.restype = i
+    lib.gattn_fwd_strided.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, vp]
+    lib.gattn_fwd_strided.restype = i
+    lib.gattn_bwd_strided.argtypes = [vp] * 9 + [i, i, i, i, f, i, vp, sz, vp, vp, vp, vp]
+    lib.gattn_bwd_strided.restype = i
     lib.gattn_status_string.argtypes = [i]
     lib.gattn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -161,6 +165,108 @@ def gattn_bwd_dkdv(q, k, v, dO, dk, dv, scale: float, workspace, stream=None) ->
                               _dev(workspace, "workspace"),
                               workspace.numel() * workspace.element_size(), _stream(stream)),
            "gattn_bwd_dkdv")
+
+
+def _view(t, name: str, shape, dtype):
+    """Pointer and {batch, head, row} element strides of a (B, H, T, hs) view
+    whose last dimension is contiguous."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name}: the head dimension must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()), tuple(int(x) for x in t.stride()[:3])
+
+
+def _strides_arg(views, group: str):
+    st = {v[1] for v in views}
+    if len(st) != 1:
+        raise ValueError(f"{group} must share one set of strides, got {sorted(st)}")
+    return (ctypes.c_int64 * 3)(*st.pop())
+
+
+def gattn_fwd_strided(q, k, v, o, lse, scale: float, stream=None) -> None:
+    """As gattn_fwd for (B, H, T, hs) views with any strides (hs contiguous):
+    q, k, v share one stride set, o has its own; lse is contiguous (B, H, T)."""
+    lib = load_library()
+    B, H, T, hs = _shape4(q)
+    dt = _dtype_code(q)
+    qkv = [_view(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+    ov = _view(o, "o", q.shape, q.dtype)
+    lp = None if lse is None else _dev(lse, "lse", (B, H, T), _torch().float32)
+    _check(lib.gattn_fwd_strided(*(p for p, _ in qkv), ov[0], lp, B, H, T, hs, float(scale), dt,
+                                 _strides_arg(qkv, "q, k, v"), _strides_arg([ov], "o"),
+                                 _stream(stream)), "gattn_fwd_strided")
+
+
+def gattn_bwd_strided(q, k, v, o, dO, lse, dq, dk, dv, scale: float, workspace,
+                      stream=None) -> None:
+    """As gattn_bwd for strided (B, H, T, hs) views: q, k, v share one stride
+    set, o and dO another, dq, dk, dv a third."""
+    lib = load_library()
+    B, H, T, hs = _shape4(q)
+    dt = _dtype_code(q)
+    qkv = [_view(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+    od = [_view(x, n, q.shape, q.dtype) for x, n in ((o, "o"), (dO, "dO"))]
+    gr = [_view(x, n, q.shape, q.dtype) for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    lp = _dev(lse, "lse", (B, H, T), _torch().float32)
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.gattn_bwd_strided(*(p for p, _ in qkv), *(p for p, _ in od), lp,
+                                 *(p for p, _ in gr), B, H, T, hs, float(scale), dt, ws, nbytes,
+                                 _strides_arg(qkv, "q, k, v"), _strides_arg(od, "o, dO"),
+                                 _strides_arg(gr, "dq, dk, dv"), _stream(stream)),
+           "gattn_bwd_strided")
+
+
+def _qkv_views(qkv, n_head: int):
+    """(B, H, T, hs) views of q, k, v inside a (B, T, 3C) projection output."""
+    B, T, C3 = (int(x) for x in qkv.shape)
+    if C3 % (3 * n_head):
+        raise ValueError("last dimension must be 3 * n_head * hs")
+    hs = C3 // (3 * n_head)
+    v4 = qkv.view(B, T, 3, n_head, hs)
+    return tuple(v4[:, :, j].transpose(1, 2) for j in range(3))
+
+
+def attention_forward_qkv(qkv, n_head: int, scale=None, need_lse: bool = True, stream=None):
+    """Causal attention of a GPT block straight from the fused projection
+    output qkv (B, T, 3C), contiguous: returns y (B, T, C) (heads side by side,
+    the layout the output projection reads) and lse (B, H, T) or None."""
+    torch = _torch()
+    if not qkv.is_contiguous():
+        raise ValueError("qkv must be contiguous (B, T, 3C)")
+    q, k, v = _qkv_views(qkv, n_head)
+    B, H, T, hs = _shape4(q)
+    y = torch.empty((B, T, H * hs), dtype=qkv.dtype, device=qkv.device)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=qkv.device) if need_lse else None
+    gattn_fwd_strided(q, k, v, y.view(B, T, H, hs).transpose(1, 2), lse,
+                      _default_scale(hs, scale), stream)
+    return y, lse
+
+
+def attention_backward_qkv(qkv, y, dy, lse, n_head: int, scale=None, workspace=None,
+                           stream=None):
+    """Gradient of attention_forward_qkv: from y and dy (B, T, C), returns
+    dqkv (B, T, 3C), the gradient of the fused projection output."""
+    torch = _torch()
+    if not (qkv.is_contiguous() and y.is_contiguous() and dy.is_contiguous()):
+        raise ValueError("qkv, y and dy must be contiguous")
+    q, k, v = _qkv_views(qkv, n_head)
+    B, H, T, hs = _shape4(q)
+    if workspace is None:
+        n = gattn_bwd_workspace_bytes(B, H, T, hs, _dtype_code(q))
+        workspace = torch.empty(n, dtype=torch.uint8, device=qkv.device)
+    dqkv = torch.empty_like(qkv)
+    dq, dk, dv = _qkv_views(dqkv, n_head)
+    o4 = y.view(B, T, H, hs).transpose(1, 2)
+    do4 = dy.view(B, T, H, hs).transpose(1, 2)
+    gattn_bwd_strided(q, k, v, o4, do4, lse, dq, dk, dv, _default_scale(hs, scale), workspace,
+                      stream)
+    return dqkv
 
 
 def _default_scale(hs: int, scale):

@@ -19,9 +19,10 @@
 //
 // Both kernels stream tiles into double-buffered, swizzled LDS tiles by LDS
 // DMA (no register staging) with one barrier per step: the DMA for step t+1
-// runs while step t computes.  Global accesses go through buffer resources
-// sized to one (b, h) slice, so rows past T read as zero and their stores are
-// dropped.  A query row past T then has zero q and dO rows (and D = lse = 0):
+// runs while step t computes.  Tensors are addressed through Layout strides
+// (q, k, v: li; o, dO: lo; dq, dk, dv: lg), and global accesses go through
+// buffer resources sized to the span of one (b, h) slice, so rows past T read
+// as zero and their stores are dropped.  A query row past T then has zero q and dO rows (and D = lse = 0):
 // its P is 1, but its dP, dS and dO are 0, so it adds exactly nothing.
 #include <cmath>
 
@@ -54,15 +55,18 @@ __global__ __launch_bounds__(kThreads) void bf16_pre_kernel(const uint16_t* __re
                                                            const uint16_t* __restrict__ dO,
                                                            const float* __restrict__ lse,
                                                            float* __restrict__ D,
-                                                           float* __restrict__ L2, long rows) {
+                                                           float* __restrict__ L2, long rows,
+                                                           int H, int T, Layout lo) {
   constexpr int TPR = HS / 8;
   const long gid = long(blockIdx.x) * kThreads + threadIdx.x;
   const long row = gid / TPR;
   const int part = int(gid % TPR);
   float s = 0.f;
   if (row < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * HS + part * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + row * HS + part * 8);
+    const int bh = int(row / T);
+    const int64_t off = slice_offset(lo, bh, H) + (row - long(bh) * T) * lo.st + part * 8;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + off);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + off);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       s = fmaf(bf16lo(a[w]), bf16lo(b[w]), s);
@@ -197,12 +201,16 @@ __device__ inline void dkdv_step_diag(const uint16_t* Qb, const uint16_t* Gb, co
   }
 }
 
-template <int HS>
+// STRIDED = false: every tensor is contiguous (B, H, T, hs) and the row
+// strides are the compile-time HS (the strides' registers and multiplies
+// would otherwise push this kernel into spills).
+template <int HS, bool STRIDED>
 __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void bf16_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
     const float* __restrict__ Dg, const float* __restrict__ L2g, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int BH, int T, float scale) {
+    uint16_t* __restrict__ dv, int BH, int H, int T, float scale, Layout li, Layout lo,
+    Layout lg) {
   using C = DkdvCfg<HS>;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[C::NS][C::BQ * HS];
   __shared__ __attribute__((aligned(16))) uint16_t Gs[C::NS][C::BQ * HS];
@@ -214,10 +222,13 @@ __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void bf16_dkdv_kernel(
   // Key tiles near the start have the most query tiles below the diagonal.
   const int kt = int(blockIdx.x) / BH;
   const int bh = int(blockIdx.x) % BH;
-  const long base = long(bh) * T * HS;
-  const uint32_t slice_bytes = uint32_t(T) * HS * 2;
+  const int64_t base = slice_base<HS, STRIDED>(li, bh, H, T);
+  const uint32_t slice_bytes = slice_bytes_of<HS, STRIDED>(li, T);
+  const int rs = STRIDED ? int(li.st) : HS, rso = STRIDED ? int(lo.st) : HS;
   const rsrc_t rq = make_rsrc(q + base, slice_bytes), rk = make_rsrc(k + base, slice_bytes);
-  const rsrc_t rv = make_rsrc(v + base, slice_bytes), rg = make_rsrc(dO + base, slice_bytes);
+  const rsrc_t rv = make_rsrc(v + base, slice_bytes);
+  const rsrc_t rg = make_rsrc(dO + slice_base<HS, STRIDED>(lo, bh, H, T),
+                              slice_bytes_of<HS, STRIDED>(lo, T));
   const rsrc_t rl = make_rsrc(L2g + long(bh) * T, uint32_t(T) * 4);
   const rsrc_t rd = make_rsrc(Dg + long(bh) * T, uint32_t(T) * 4);
 
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void bf16_dkdv_kernel(
   DkdvRegs<HS> R;
 #pragma unroll
   for (int ks = 0; ks < C::KSTEP; ++ks) {
-    const uint32_t off = uint32_t(krow * HS + 16 * ks + 8 * h) * 2;
+    const uint32_t off = uint32_t(krow * rs + 16 * ks + 8 * h) * 2;
     R.kf[ks] = bload16(rk, off);
     R.vf[ks] = bload16(rv, off);
   }
@@ -238,8 +249,8 @@ __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void bf16_dkdv_kernel(
 
   constexpr int QQ = C::BQ / C::NW;  // lse / D rows per wavefront
   auto issue = [&](int qt, int buf) {
-    dma_tile<HS, C::BQ, C::NW>(rq, qt * C::BQ, Qs[buf], w, lane);
-    dma_tile<HS, C::BQ, C::NW>(rg, qt * C::BQ, Gs[buf], w, lane);
+    dma_tile<HS, C::BQ, C::NW>(rq, qt * C::BQ, rs, Qs[buf], w, lane);
+    dma_tile<HS, C::BQ, C::NW>(rg, qt * C::BQ, rso, Gs[buf], w, lane);
     const uint32_t off = uint32_t(qt * C::BQ + w * QQ) * 4;
     dma_f32(rl, off, Ls[buf] + w * QQ, QQ, lane);
     dma_f32(rd, off, Ds[buf] + w * QQ, QQ, lane);
@@ -270,12 +281,15 @@ __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void bf16_dkdv_kernel(
   ring_loop<C::NS>(nsteps, step);
 
   // dK^T / dV^T register i of lane (n, h): column d = db*32 + 8*(i/4) + 4h + i%4, key krow.
-  const rsrc_t wk = make_rsrc(dk + base, slice_bytes), wv = make_rsrc(dv + base, slice_bytes);
+  const int64_t gbase = slice_base<HS, STRIDED>(lg, bh, H, T);
+  const uint32_t gbytes = slice_bytes_of<HS, STRIDED>(lg, T);
+  const rsrc_t wk = make_rsrc(dk + gbase, gbytes), wv = make_rsrc(dv + gbase, gbytes);
+  const int rsg = STRIDED ? int(lg.st) : HS;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t off = uint32_t(krow * HS + db * 32 + 8 * g + 4 * h) * 2;
+      const uint32_t off = uint32_t(krow * rsg + db * 32 + 8 * g + 4 * h) * 2;
       bstore8(wv, off, u32x2{pack_bf16(R.dva[db][4 * g], R.dva[db][4 * g + 1]),
                              pack_bf16(R.dva[db][4 * g + 2], R.dva[db][4 * g + 3])});
       bstore8(wk, off, u32x2{pack_bf16(R.dka[db][4 * g] * scale, R.dka[db][4 * g + 1] * scale),
@@ -363,12 +377,13 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
   }
 }
 
-template <int HS>
+template <int HS, bool STRIDED>  // STRIDED as for the dK/dV kernel
 __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, float* __restrict__ Dg,
-    float* __restrict__ L2g, uint16_t* __restrict__ dq, int BH, int T, float scale) {
+    float* __restrict__ L2g, uint16_t* __restrict__ dq, int BH, int H, int T, float scale,
+    Layout li, Layout lo, Layout lg) {
   using C = DqCfg<HS>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[C::NS][C::BN * HS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[C::NS][C::BN * HS];
@@ -378,11 +393,14 @@ __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
   const int nqt = (T + C::BM - 1) / C::BM;
   const int qt = nqt - 1 - int(blockIdx.x) / BH;  // heaviest query tiles first
   const int bh = int(blockIdx.x) % BH;
-  const long base = long(bh) * T * HS;
-  const uint32_t slice_bytes = uint32_t(T) * HS * 2;
+  const int64_t base = slice_base<HS, STRIDED>(li, bh, H, T);
+  const uint32_t slice_bytes = slice_bytes_of<HS, STRIDED>(li, T);
+  const int rs = STRIDED ? int(li.st) : HS, rso = STRIDED ? int(lo.st) : HS;
   const rsrc_t rq = make_rsrc(q + base, slice_bytes), rk = make_rsrc(k + base, slice_bytes);
-  const rsrc_t rv = make_rsrc(v + base, slice_bytes), rg = make_rsrc(dO + base, slice_bytes);
-  const rsrc_t ro = make_rsrc(o + base, slice_bytes);
+  const rsrc_t rv = make_rsrc(v + base, slice_bytes);
+  const int64_t obase = slice_base<HS, STRIDED>(lo, bh, H, T);
+  const uint32_t obytes = slice_bytes_of<HS, STRIDED>(lo, T);
+  const rsrc_t rg = make_rsrc(dO + obase, obytes), ro = make_rsrc(o + obase, obytes);
 
   const int r0 = qt * C::BM;
   const int q0 = r0 + 32 * w;
@@ -391,8 +409,8 @@ __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
   const float c = scale * kLog2e;
 
   auto issue = [&](int kt, int buf) {
-    dma_tile<HS, C::BN, C::NW>(rk, kt * C::BN, Ks[buf], w, lane);
-    dma_tile<HS, C::BN, C::NW>(rv, kt * C::BN, Vs[buf], w, lane);
+    dma_tile<HS, C::BN, C::NW>(rk, kt * C::BN, rs, Ks[buf], w, lane);
+    dma_tile<HS, C::BN, C::NW>(rv, kt * C::BN, rs, Vs[buf], w, lane);
   };
   const int nkt = (min(r0 + C::BM, T) - 1) / C::BN + 1;
 #pragma unroll
@@ -405,10 +423,11 @@ __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
   float dpart = 0.f;
 #pragma unroll
   for (int ks = 0; ks < C::KSTEP; ++ks) {
-    const uint32_t off = uint32_t(qrow * HS + 16 * ks + 8 * h) * 2;
-    qf[ks] = bload16(rq, off);
-    gf[ks] = bload16(rg, off);
-    const u32x4 of = bload16(ro, off);
+    const uint32_t col = uint32_t(16 * ks + 8 * h);
+    qf[ks] = bload16(rq, (uint32_t(qrow * rs) + col) * 2);
+    const uint32_t offo = (uint32_t(qrow * rso) + col) * 2;
+    gf[ks] = bload16(rg, offo);
+    const u32x4 of = bload16(ro, offo);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       dpart = fmaf(bf16lo(of[e]), bf16lo(gf[ks][e]), dpart);
@@ -449,12 +468,14 @@ __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
   ring_loop<C::NS>(nkt, step);
 
   // dQ^T register i of lane (n, h): column d = db*32 + 8*(i/4) + 4h + i%4, query qrow.
-  const rsrc_t wq = make_rsrc(dq + base, slice_bytes);
+  const rsrc_t wq = make_rsrc(dq + slice_base<HS, STRIDED>(lg, bh, H, T),
+                              slice_bytes_of<HS, STRIDED>(lg, T));
+  const int rsg = STRIDED ? int(lg.st) : HS;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t off = uint32_t(qrow * HS + db * 32 + 8 * g + 4 * h) * 2;
+      const uint32_t off = uint32_t(qrow * rsg + db * 32 + 8 * g + 4 * h) * 2;
       bstore8(wq, off, u32x2{pack_bf16(dqa[db][4 * g] * scale, dqa[db][4 * g + 1] * scale),
                              pack_bf16(dqa[db][4 * g + 2] * scale, dqa[db][4 * g + 3] * scale)});
     }
@@ -463,37 +484,39 @@ __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
 }  // namespace
 
 hipError_t bf16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                        float* L2, int BH, int T, int hs, hipStream_t s) {
+                        float* L2, int BH, int H, int T, int hs, Layout lo, hipStream_t s) {
   const long rows = long(BH) * T;
   const long threads = rows * (hs / 8);
   const dim3 grid(unsigned((threads + kThreads - 1) / kThreads));
-  if (hs == 64) return launch(bf16_pre_kernel<64>, grid, dim3(kThreads), s, o, dO, lse, D, L2, rows);
-  return launch(bf16_pre_kernel<32>, grid, dim3(kThreads), s, o, dO, lse, D, L2, rows);
+  if (hs == 64)
+    return launch(bf16_pre_kernel<64>, grid, dim3(kThreads), s, o, dO, lse, D, L2, rows, H, T, lo);
+  return launch(bf16_pre_kernel<32>, grid, dim3(kThreads), s, o, dO, lse, D, L2, rows, H, T, lo);
 }
 
 hipError_t bf16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
-                         uint16_t* dv, int BH, int T, int hs, float scale, hipStream_t s) {
+                         uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
+                         Layout lo, Layout lg, hipStream_t s) {
   const int bn = DkdvCfg<64>::BN;
   const dim3 grid(unsigned(((T + bn - 1) / bn) * BH));
-  if (hs == 64)
-    return launch(bf16_dkdv_kernel<64>, grid, dim3(kThreads), s, q, k, v, dO, D, L2, dk, dv, BH,
-                  T, scale);
-  return launch(bf16_dkdv_kernel<32>, grid, dim3(kThreads), s, q, k, v, dO, D, L2, dk, dv, BH, T,
-                scale);
+  const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
+  auto kern = hs == 64 ? (strided ? bf16_dkdv_kernel<64, true> : bf16_dkdv_kernel<64, false>)
+                       : (strided ? bf16_dkdv_kernel<32, true> : bf16_dkdv_kernel<32, false>);
+  return launch(kern, grid, dim3(kThreads), s, q, k, v, dO, D, L2, dk, dv, BH, H, T, scale, li, lo,
+                lg);
 }
 
 hipError_t bf16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                       float* L2, uint16_t* dq, int BH, int T, int hs, float scale,
-                       hipStream_t s) {
+                       float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
+                       Layout li, Layout lo, Layout lg, hipStream_t s) {
   const int bm = DqCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
-  if (hs == 64)
-    return launch(bf16_dq_kernel<64>, grid, dim3(kThreads), s, q, k, v, o, dO, lse, D, L2, dq,
-                  BH, T, scale);
-  return launch(bf16_dq_kernel<32>, grid, dim3(kThreads), s, q, k, v, o, dO, lse, D, L2, dq, BH,
-                T, scale);
+  const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
+  auto kern = hs == 64 ? (strided ? bf16_dq_kernel<64, true> : bf16_dq_kernel<64, false>)
+                       : (strided ? bf16_dq_kernel<32, true> : bf16_dq_kernel<32, false>);
+  return launch(kern, grid, dim3(kThreads), s, q, k, v, o, dO, lse, D, L2, dq, BH, H, T, scale, li,
+                lo, lg);
 }
 
 }  // namespace gattn

@@ -162,11 +162,12 @@ __device__ inline u32x4 op_tr(const uint16_t* tile, const LaneOffsets<HS>& L, in
 // with no register staging.  Lane L of DMA instruction i fills chunk position
 // L % (HS/8) of tile row i*(512/HS) + L/(HS/8), so it fetches the global chunk
 // that the swizzle puts there.  Rows past the buffer resource's end arrive as
-// zeros.  ROWS rows starting at global row row0 of the resource; the NW
-// wavefronts of the workgroup share the instructions.  The caller waits
-// (s_waitcnt vmcnt) and synchronises before reading the tile.
+// zeros.  ROWS rows starting at global row row0 of the resource, whose rows
+// are `st` elements apart; the NW wavefronts of the workgroup share the
+// instructions.  The caller waits (s_waitcnt vmcnt) and synchronises before
+// reading the tile.
 template <int HS, int ROWS, int NW>
-__device__ inline void dma_tile(rsrc_t r, int row0, uint16_t* tile, int w, int lane) {
+__device__ inline void dma_tile(rsrc_t r, int row0, int st, uint16_t* tile, int w, int lane) {
   constexpr int RPI = 512 / HS;  // rows per DMA instruction (1 KB)
   constexpr int NI = ROWS / RPI;
   static_assert(NI * RPI == ROWS, "tile rows");
@@ -174,7 +175,7 @@ __device__ inline void dma_tile(rsrc_t r, int row0, uint16_t* tile, int w, int l
   for (int i = w; i < NI; i += NW) {
     const int rl = i * RPI + lane / (HS / 8);
     const int c = (lane % (HS / 8)) ^ swz<HS>(rl);
-    const uint32_t off = uint32_t((row0 + rl) * HS + c * 8) * 2;
+    const uint32_t off = uint32_t((row0 + rl) * st + c * 8) * 2;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(tile + i * 512), 16, off, 0, 0, 0);
   }
@@ -212,6 +213,20 @@ __device__ inline void ring_block(int t0, int n, F& step) {
 template <int NS, class F>
 __device__ inline void ring_loop(int n, F& step) {
   for (int t0 = 0; t0 < n; t0 += NS) ring_block<0, NS>(t0, n, step);
+}
+
+// Element offset and byte span of slice bh of a tensor: through its Layout,
+// or, when STRIDED is false (contiguous (B, H, T, HS)), as bh*T*HS and T*HS*2
+// without the layout's division by H.
+template <int HS, bool STRIDED, class L>
+__device__ inline int64_t slice_base(const L& l, int bh, int H, int T) {
+  if constexpr (STRIDED) return slice_offset(l, bh, H);
+  return int64_t(bh) * T * HS;
+}
+template <int HS, bool STRIDED, class L>
+__device__ inline uint32_t slice_bytes_of(const L& l, int T) {
+  if constexpr (STRIDED) return slice_span_bytes(l, T, HS, 2);
+  return uint32_t(T) * HS * 2;
 }
 
 // Ring of NS LDS stages fed by DMA: before computing step t, step t+NS-1 is

@@ -25,9 +25,12 @@
 //                                   accumulators (no LDS round trip), V^T
 //                                   read from the row-major V tile with LDS
 //                                   transpose reads.
-// Rows past T are read as zeros (buffer resources sized to one (b, h)
-// slice); keys past T are always above the diagonal of every real query, so
-// the mask removes them, and stores of rows past T are dropped.
+// Tensors are addressed through Layout strides (q, k, v: li; o: lo), so the
+// fused (B, T, 3C) projection output and a (B, T, C) output are read and
+// written in place.  Rows past T are read as zeros (buffer resources sized to
+// the span of one (b, h) slice); keys past T are always above the diagonal of
+// every real query, so the mask removes them, and stores of rows past T are
+// dropped.
 #include <cmath>
 
 #include "bf16_common.h"
@@ -136,13 +139,16 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb,
         st.oacc[db] = mfma32(op_tr<HS>(Vb, L, kh * 32 + 16 * t, db), pf[kh][t], st.oacc[db]);
 }
 
-template <int HS>
+// STRIDED = false: q, k, v and o are contiguous (B, H, T, hs) and the row
+// strides are the compile-time HS.
+template <int HS, bool STRIDED>
 __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
                                                            uint16_t* __restrict__ o,
-                                                           float* __restrict__ lse, int BH, int T,
-                                                           float scale) {
+                                                           float* __restrict__ lse, int BH, int H,
+                                                           int T, float scale, Layout li,
+                                                           Layout lo) {
   using C = FwdCfg<HS>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[C::NS][C::BN * HS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[C::NS][C::BN * HS];
@@ -153,8 +159,9 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
   // Heaviest query tiles (most key tiles under the diagonal) first.
   const int qt = nqt - 1 - int(blockIdx.x) / BH;
   const int bh = int(blockIdx.x) % BH;
-  const long base = long(bh) * T * HS;
-  const uint32_t slice_bytes = uint32_t(T) * HS * 2;
+  const int64_t base = slice_base<HS, STRIDED>(li, bh, H, T);
+  const uint32_t slice_bytes = slice_bytes_of<HS, STRIDED>(li, T);
+  const int rs = STRIDED ? int(li.st) : HS;
   const rsrc_t rq = make_rsrc(q + base, slice_bytes), rk = make_rsrc(k + base, slice_bytes);
   const rsrc_t rv = make_rsrc(v + base, slice_bytes);
 
@@ -165,8 +172,8 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
   const float c = scale * kLog2e;
 
   auto issue = [&](int kt, int buf) {
-    dma_tile<HS, C::BN, C::NW>(rk, kt * C::BN, Ks[buf], w, lane);
-    dma_tile<HS, C::BN, C::NW>(rv, kt * C::BN, Vs[buf], w, lane);
+    dma_tile<HS, C::BN, C::NW>(rk, kt * C::BN, rs, Ks[buf], w, lane);
+    dma_tile<HS, C::BN, C::NW>(rv, kt * C::BN, rs, Vs[buf], w, lane);
   };
 #pragma unroll
   for (int j = 0; j < C::NS - 1; ++j)
@@ -176,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
   u32x4 qf[C::KSTEP];
 #pragma unroll
   for (int ks = 0; ks < C::KSTEP; ++ks)
-    qf[ks] = bload16(rq, uint32_t(qrow * HS + 16 * ks + 8 * h) * 2);
+    qf[ks] = bload16(rq, uint32_t(qrow * rs + 16 * ks + 8 * h) * 2);
 
   FwdState<HS> st;
 #pragma unroll
@@ -212,12 +219,14 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
   // d = db*32 + 8*(i/4) + 4h + i%4 of row qrow.
   const float lt = halves_sum(st.l);
   const float inv = 1.f / lt;
-  const rsrc_t wo = make_rsrc(o + base, slice_bytes);
+  const rsrc_t wo = make_rsrc(o + slice_base<HS, STRIDED>(lo, bh, H, T),
+                              slice_bytes_of<HS, STRIDED>(lo, T));
+  const int rso = STRIDED ? int(lo.st) : HS;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const uint32_t off = uint32_t(qrow * HS + db * 32 + 8 * g + 4 * h) * 2;
+      const uint32_t off = uint32_t(qrow * rso + db * 32 + 8 * g + 4 * h) * 2;
       bstore8(wo, off, u32x2{pack_bf16(st.oacc[db][4 * g] * inv, st.oacc[db][4 * g + 1] * inv),
                              pack_bf16(st.oacc[db][4 * g + 2] * inv, st.oacc[db][4 * g + 3] * inv)});
     }
@@ -229,12 +238,14 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
 }  // namespace
 
 hipError_t bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                    float* lse, int BH, int T, int hs, float scale, hipStream_t s) {
+                    float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
+                    hipStream_t s) {
   const int bm = FwdCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
-  if (hs == 64)
-    return launch(bf16_fwd_kernel<64>, grid, dim3(kThreads), s, q, k, v, o, lse, BH, T, scale);
-  return launch(bf16_fwd_kernel<32>, grid, dim3(kThreads), s, q, k, v, o, lse, BH, T, scale);
+  const bool strided = !all_contiguous(H, T, hs, li, lo, lo);
+  auto kern = hs == 64 ? (strided ? bf16_fwd_kernel<64, true> : bf16_fwd_kernel<64, false>)
+                       : (strided ? bf16_fwd_kernel<32, true> : bf16_fwd_kernel<32, false>);
+  return launch(kern, grid, dim3(kThreads), s, q, k, v, o, lse, BH, H, T, scale, li, lo);
 }
 
 }  // namespace gattn

@@ -7,6 +7,10 @@
 // result is independent of launch order: the path is deterministic and uses
 // no atomics.
 //
+// Tensors are addressed through Layout strides (rows of hs contiguous
+// elements): q, k, v share layout li, o and dO share lo, dq, dk, dv share lg;
+// lse, D and L2 are contiguous (B, H, T).
+//
 // Per row i (query) or column j (key) of one (b, h) slice:
 //   forward  : online softmax over keys j <= i (tril mask, "Let's build GPT"
 //              summary page 48:54 / 55:20; softmax rows 51:04), scores scaled
@@ -60,21 +64,23 @@ __device__ inline float row_dot(const float (&a)[NPL], const float* __restrict__
 template <int NPL>
 __global__ __launch_bounds__(64 * kWaves) void f32_fwd_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int BH, int T, int hs, float scale) {
+    float* __restrict__ o, float* __restrict__ lse, int BH, int H, int T, int hs, float scale,
+    Layout li, Layout lo) {
   const int lane = threadIdx.x & 63;
   const long row = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (row >= long(BH) * T) return;  // uniform per wavefront
-  const long bh = row / T;
-  const int i = int(row - bh * T);
-  const float* kb = k + bh * T * hs;
-  const float* vb = v + bh * T * hs;
+  const int bh = int(row / T);
+  const int i = int(row - long(bh) * T);
+  const int64_t si = slice_offset(li, bh, H);
+  const float* kb = k + si;
+  const float* vb = v + si;
   float qr[NPL], acc[NPL];
-  load_row<NPL>(q + row * hs, hs, lane, qr);
+  load_row<NPL>(q + si + i * li.st, hs, lane, qr);
 #pragma unroll
   for (int e = 0; e < NPL; ++e) acc[e] = 0.f;
   float m = -INFINITY, l = 0.f;
   for (int j = 0; j <= i; ++j) {
-    const float s = wave_sum(row_dot<NPL>(qr, kb + long(j) * hs, hs, lane)) * scale;
+    const float s = wave_sum(row_dot<NPL>(qr, kb + j * li.st, hs, lane)) * scale;
     const float mn = fmaxf(m, s);
     const float alpha = expf(m - mn);  // m = -inf on the first key: alpha = 0
     const float p = expf(s - mn);
@@ -82,16 +88,17 @@ __global__ __launch_bounds__(64 * kWaves) void f32_fwd_kernel(
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
       int d = lane + 64 * e;
-      float vv = d < hs ? vb[long(j) * hs + d] : 0.f;
+      float vv = d < hs ? vb[j * li.st + d] : 0.f;
       acc[e] = fmaf(p, vv, acc[e] * alpha);
     }
     m = mn;
   }
   const float inv = 1.f / l;
+  float* orow = o + slice_offset(lo, bh, H) + i * lo.st;
 #pragma unroll
   for (int e = 0; e < NPL; ++e) {
     int d = lane + 64 * e;
-    if (d < hs) o[row * hs + d] = acc[e] * inv;
+    if (d < hs) orow[d] = acc[e] * inv;
   }
   if (lse != nullptr && lane == 0) lse[row] = m + logf(l);
 }
@@ -100,13 +107,16 @@ __global__ __launch_bounds__(64 * kWaves) void f32_fwd_kernel(
 template <int NPL>
 __global__ __launch_bounds__(64 * kWaves) void f32_pre_kernel(
     const float* __restrict__ o, const float* __restrict__ dO, const float* __restrict__ lse,
-    float* __restrict__ D, float* __restrict__ L2, int BH, int T, int hs) {
+    float* __restrict__ D, float* __restrict__ L2, int BH, int H, int T, int hs, Layout lo) {
   const int lane = threadIdx.x & 63;
   const long row = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (row >= long(BH) * T) return;
+  const int bh = int(row / T);
+  const int i = int(row - long(bh) * T);
+  const int64_t off = slice_offset(lo, bh, H) + i * lo.st;
   float a[NPL];
-  load_row<NPL>(dO + row * hs, hs, lane, a);
-  const float s = wave_sum(row_dot<NPL>(a, o + row * hs, hs, lane));
+  load_row<NPL>(dO + off, hs, lane, a);
+  const float s = wave_sum(row_dot<NPL>(a, o + off, hs, lane));
   if (lane == 0) {
     D[row] = s;
     L2[row] = lse[row] * 1.4426950408889634f;
@@ -119,41 +129,45 @@ template <int NPL>
 __global__ __launch_bounds__(64 * kWaves) void f32_dkdv_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ dO, const float* __restrict__ D, const float* __restrict__ L2,
-    float* __restrict__ dk, float* __restrict__ dv, int BH, int T, int hs, float scale) {
+    float* __restrict__ dk, float* __restrict__ dv, int BH, int H, int T, int hs, float scale,
+    Layout li, Layout lo, Layout lg) {
   const float c = scale * 1.4426950408889634f;
   const int lane = threadIdx.x & 63;
   const long row = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (row >= long(BH) * T) return;
-  const long bh = row / T;
-  const int j = int(row - bh * T);
-  const float* qb = q + bh * T * hs;
-  const float* ob = dO + bh * T * hs;
+  const int bh = int(row / T);
+  const int j = int(row - long(bh) * T);
+  const int64_t si = slice_offset(li, bh, H);
+  const float* qb = q + si;
+  const float* ob = dO + slice_offset(lo, bh, H);
+  const long rb = long(bh) * T;  // row base of the (B, H, T) vectors
   float kr[NPL], vr[NPL], ak[NPL], av[NPL];
-  load_row<NPL>(k + row * hs, hs, lane, kr);
-  load_row<NPL>(v + row * hs, hs, lane, vr);
+  load_row<NPL>(k + si + j * li.st, hs, lane, kr);
+  load_row<NPL>(v + si + j * li.st, hs, lane, vr);
 #pragma unroll
   for (int e = 0; e < NPL; ++e) ak[e] = av[e] = 0.f;
   for (int i = j; i < T; ++i) {
-    float s = row_dot<NPL>(kr, qb + long(i) * hs, hs, lane);
-    float dp = row_dot<NPL>(vr, ob + long(i) * hs, hs, lane);
+    float s = row_dot<NPL>(kr, qb + i * li.st, hs, lane);
+    float dp = row_dot<NPL>(vr, ob + i * lo.st, hs, lane);
     wave_sum2(s, dp);
-    const float p = exp2f(fmaf(s, c, -L2[bh * T + i]));
-    const float ds = p * (dp - D[bh * T + i]);
+    const float p = exp2f(fmaf(s, c, -L2[rb + i]));
+    const float ds = p * (dp - D[rb + i]);
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
       int d = lane + 64 * e;
-      float qq = d < hs ? qb[long(i) * hs + d] : 0.f;
-      float gg = d < hs ? ob[long(i) * hs + d] : 0.f;
+      float qq = d < hs ? qb[i * li.st + d] : 0.f;
+      float gg = d < hs ? ob[i * lo.st + d] : 0.f;
       av[e] = fmaf(p, gg, av[e]);
       ak[e] = fmaf(ds, qq, ak[e]);
     }
   }
+  const int64_t go = slice_offset(lg, bh, H) + j * lg.st;
 #pragma unroll
   for (int e = 0; e < NPL; ++e) {
     int d = lane + 64 * e;
     if (d < hs) {
-      dk[row * hs + d] = ak[e] * scale;
-      dv[row * hs + d] = av[e];
+      dk[go + d] = ak[e] * scale;
+      dv[go + d] = av[e];
     }
   }
 }
@@ -163,37 +177,40 @@ template <int NPL>
 __global__ __launch_bounds__(64 * kWaves) void f32_dq_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ D,
-    float* __restrict__ dq, int BH, int T, int hs, float scale) {
+    float* __restrict__ dq, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
+    Layout lg) {
   const int lane = threadIdx.x & 63;
   const long row = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (row >= long(BH) * T) return;
-  const long bh = row / T;
-  const int i = int(row - bh * T);
-  const float* kb = k + bh * T * hs;
-  const float* vb = v + bh * T * hs;
+  const int bh = int(row / T);
+  const int i = int(row - long(bh) * T);
+  const int64_t si = slice_offset(li, bh, H);
+  const float* kb = k + si;
+  const float* vb = v + si;
   float qr[NPL], gr[NPL], aq[NPL];
-  load_row<NPL>(q + row * hs, hs, lane, qr);
-  load_row<NPL>(dO + row * hs, hs, lane, gr);
+  load_row<NPL>(q + si + i * li.st, hs, lane, qr);
+  load_row<NPL>(dO + slice_offset(lo, bh, H) + i * lo.st, hs, lane, gr);
 #pragma unroll
   for (int e = 0; e < NPL; ++e) aq[e] = 0.f;
-  const float li = lse[row], Di = D[row];
+  const float li_ = lse[row], Di = D[row];
   for (int j = 0; j <= i; ++j) {
-    float s = row_dot<NPL>(qr, kb + long(j) * hs, hs, lane);
-    float dp = row_dot<NPL>(gr, vb + long(j) * hs, hs, lane);
+    float s = row_dot<NPL>(qr, kb + j * li.st, hs, lane);
+    float dp = row_dot<NPL>(gr, vb + j * li.st, hs, lane);
     wave_sum2(s, dp);
-    const float p = expf(s * scale - li);
+    const float p = expf(s * scale - li_);
     const float ds = p * (dp - Di);
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
       int d = lane + 64 * e;
-      float kk = d < hs ? kb[long(j) * hs + d] : 0.f;
+      float kk = d < hs ? kb[j * li.st + d] : 0.f;
       aq[e] = fmaf(ds, kk, aq[e]);
     }
   }
+  float* qrow = dq + slice_offset(lg, bh, H) + i * lg.st;
 #pragma unroll
   for (int e = 0; e < NPL; ++e) {
     int d = lane + 64 * e;
-    if (d < hs) dq[row * hs + d] = aq[e] * scale;
+    if (d < hs) qrow[d] = aq[e] * scale;
   }
 }
 
@@ -205,41 +222,42 @@ dim3 rows_grid(int BH, int T) {
 }  // namespace
 
 hipError_t f32_fwd(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
-                   int T, int hs, float scale, hipStream_t s) {
+                   int H, int T, int hs, float scale, Layout li, Layout lo, hipStream_t s) {
   if (hs <= 64)
     return launch(f32_fwd_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, o, lse, BH,
-                  T, hs, scale);
-  return launch(f32_fwd_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, o, lse, BH, T,
-                hs, scale);
+                  H, T, hs, scale, li, lo);
+  return launch(f32_fwd_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, o, lse, BH, H,
+                T, hs, scale, li, lo);
 }
 
 hipError_t f32_bwd_pre(const float* o, const float* dO, const float* lse, float* D, float* L2,
-                       int BH, int T, int hs, hipStream_t s) {
+                       int BH, int H, int T, int hs, Layout lo, hipStream_t s) {
   if (hs <= 64)
     return launch(f32_pre_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, o, dO, lse, D, L2, BH,
-                  T, hs);
-  return launch(f32_pre_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, o, dO, lse, D, L2, BH, T,
-                hs);
+                  H, T, hs, lo);
+  return launch(f32_pre_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, o, dO, lse, D, L2, BH, H,
+                T, hs, lo);
 }
 
 hipError_t f32_bwd_dkdv(const float* q, const float* k, const float* v, const float* dO,
-                        const float* D, const float* L2, float* dk, float* dv, int BH, int T,
-                        int hs, float scale, hipStream_t s) {
+                        const float* D, const float* L2, float* dk, float* dv, int BH, int H,
+                        int T, int hs, float scale, Layout li, Layout lo, Layout lg,
+                        hipStream_t s) {
   if (hs <= 64)
     return launch(f32_dkdv_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, D, L2,
-                  dk, dv, BH, T, hs, scale);
+                  dk, dv, BH, H, T, hs, scale, li, lo, lg);
   return launch(f32_dkdv_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, D, L2, dk,
-                dv, BH, T, hs, scale);
+                dv, BH, H, T, hs, scale, li, lo, lg);
 }
 
 hipError_t f32_bwd_dq(const float* q, const float* k, const float* v, const float* dO,
-                      const float* lse, const float* D, float* dq, int BH, int T, int hs,
-                      float scale, hipStream_t s) {
+                      const float* lse, const float* D, float* dq, int BH, int H, int T, int hs,
+                      float scale, Layout li, Layout lo, Layout lg, hipStream_t s) {
   if (hs <= 64)
     return launch(f32_dq_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D,
-                  dq, BH, T, hs, scale);
+                  dq, BH, H, T, hs, scale, li, lo, lg);
   return launch(f32_dq_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D, dq,
-                BH, T, hs, scale);
+                BH, H, T, hs, scale, li, lo, lg);
 }
 
 }  // namespace gattn

@@ -43,10 +43,112 @@ int check_main(const void* q, const void* k, const void* v, const void* dO, floa
   return check_workspace(ws, wsb, B, H, T, hs, dtype);
 }
 
+// Strides {batch, head, row} in elements for a (B, H, T, hs) tensor with
+// contiguous hs; nullptr means the contiguous layout.  Rows must not overlap
+// (row stride >= hs), every row must start on a 16-byte boundary and the
+// strides must be non-negative.  Kernels address a slice with 32-bit byte
+// offsets and touch rows up to the next tile boundary past T (fewer than 256
+// rows further), so T + 256 rows of the slice must span less than 2^31 bytes:
+// a row past T then lies past the slice's range and reads as zero.
+int layout_of(const int64_t* strides, int H, int T, int hs, int dtype, gattn::Layout& l) {
+  if (strides == nullptr) {
+    l = gattn::contiguous_layout(H, T, hs);
+    return GATTN_OK;
+  }
+  const int64_t esize = dtype == GATTN_F32 ? 4 : 2;
+  l = gattn::Layout{strides[0], strides[1], strides[2]};
+  if (l.sb < 0 || l.sh < 0 || l.st < hs) return GATTN_ERR_INVALID_ARG;
+  if ((l.sb * esize) % 16 || (l.sh * esize) % 16 || (l.st * esize) % 16) return GATTN_ERR_INVALID_ARG;
+  if ((int64_t(T) + 256) * l.st * esize >= (int64_t(1) << 31)) return GATTN_ERR_INVALID_ARG;
+  return GATTN_OK;
+}
+
 // Workspace parts: D, then L2 = lse * log2(e).
 float* ws_D(void* ws) { return static_cast<float*>(ws); }
 float* ws_L2(void* ws, int B, int H, int T) {
   return reinterpret_cast<float*>(static_cast<char*>(ws) + ws_part_bytes(B, H, T));
+}
+
+// Implementations on layouts (arguments already validated).
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int T, int hs, float scale, int dtype, gattn::Layout li, gattn::Layout lo,
+             hipStream_t stream) {
+  const int BH = B * H;
+  if (dtype == GATTN_F32)
+    return status_of(gattn::f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
+                                    static_cast<const float*>(v), static_cast<float*>(o), lse, BH,
+                                    H, T, hs, scale, li, lo, stream));
+  return status_of(gattn::bf16_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                   static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+                                   BH, H, T, hs, scale, li, lo, stream));
+}
+
+int pre_impl(const void* o, const void* dO, const float* lse, int B, int H, int T, int hs,
+             int dtype, void* workspace, gattn::Layout lo, hipStream_t stream) {
+  float* D = ws_D(workspace);
+  float* L2 = ws_L2(workspace, B, H, T);
+  if (dtype == GATTN_F32)
+    return status_of(gattn::f32_bwd_pre(static_cast<const float*>(o), static_cast<const float*>(dO),
+                                        lse, D, L2, B * H, H, T, hs, lo, stream));
+  return status_of(gattn::bf16_bwd_pre(static_cast<const uint16_t*>(o),
+                                       static_cast<const uint16_t*>(dO), lse, D, L2, B * H, H, T,
+                                       hs, lo, stream));
+}
+
+int dq_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
+            const float* lse, void* dq, int B, int H, int T, int hs, float scale, int dtype,
+            void* workspace, gattn::Layout li, gattn::Layout lo, gattn::Layout lg,
+            hipStream_t stream) {
+  float* D = ws_D(workspace);
+  float* L2 = ws_L2(workspace, B, H, T);
+  if (dtype == GATTN_F32) {
+    if (int st = pre_impl(o, dO, lse, B, H, T, hs, dtype, workspace, lo, stream)) return st;
+    return status_of(gattn::f32_bwd_dq(
+        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+        static_cast<const float*>(dO), lse, D, static_cast<float*>(dq), B * H, H, T, hs, scale, li,
+        lo, lg, stream));
+  }
+  return status_of(gattn::bf16_bwd_dq(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
+      static_cast<const uint16_t*>(dO), lse, D, L2, static_cast<uint16_t*>(dq), B * H, H, T, hs,
+      scale, li, lo, lg, stream));
+}
+
+int dkdv_impl(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
+              int B, int H, int T, int hs, float scale, int dtype, void* workspace,
+              gattn::Layout li, gattn::Layout lo, gattn::Layout lg, hipStream_t stream) {
+  const float* D = ws_D(workspace);
+  const float* L2 = ws_L2(workspace, B, H, T);
+  if (dtype == GATTN_F32)
+    return status_of(gattn::f32_bwd_dkdv(
+        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+        static_cast<const float*>(dO), D, L2, static_cast<float*>(dk), static_cast<float*>(dv),
+        B * H, H, T, hs, scale, li, lo, lg, stream));
+  return status_of(gattn::bf16_bwd_dkdv(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), D, L2,
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B * H, H, T, hs, scale, li, lo, lg,
+      stream));
+}
+
+int check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              int B, int H, int T, int hs, float scale, int dtype) {
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o)) return GATTN_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 16)) return GATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return GATTN_ERR_INVALID_ARG;
+  return check_shape(B, H, T, hs, dtype);
+}
+
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, const void* dq, const void* dk, const void* dv, int B, int H,
+              int T, int hs, float scale, int dtype, const void* ws, size_t wsb) {
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(dO) || !ptr_ok(lse) ||
+      !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv))
+    return GATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return GATTN_ERR_INVALID_ARG;
+  if (int st = check_shape(B, H, T, hs, dtype)) return st;
+  return check_workspace(ws, wsb, B, H, T, hs, dtype);
 }
 
 }  // namespace
@@ -71,18 +173,19 @@ size_t gattn_bwd_workspace_bytes(int B, int H, int T, int hs, int dtype) {
 
 int gattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
               int T, int hs, float scale, int dtype, hipStream_t stream) {
-  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o)) return GATTN_ERR_INVALID_ARG;
-  if (lse != nullptr && !aligned(lse, 16)) return GATTN_ERR_INVALID_ARG;
-  if (!scale_ok(scale)) return GATTN_ERR_INVALID_ARG;
-  if (int st = check_shape(B, H, T, hs, dtype)) return st;
-  const int BH = B * H;
-  if (dtype == GATTN_F32)
-    return status_of(gattn::f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
-                                    static_cast<const float*>(v), static_cast<float*>(o), lse, BH,
-                                    T, hs, scale, stream));
-  return status_of(gattn::bf16_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                   static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
-                                   BH, T, hs, scale, stream));
+  if (int st = check_fwd(q, k, v, o, lse, B, H, T, hs, scale, dtype)) return st;
+  const gattn::Layout c = gattn::contiguous_layout(H, T, hs);
+  return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, c, c, stream);
+}
+
+int gattn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int T, int hs, float scale, int dtype, const int64_t* qkv_strides,
+                      const int64_t* o_strides, hipStream_t stream) {
+  if (int st = check_fwd(q, k, v, o, lse, B, H, T, hs, scale, dtype)) return st;
+  gattn::Layout li, lo;
+  if (int st = layout_of(qkv_strides, H, T, hs, dtype, li)) return st;
+  if (int st = layout_of(o_strides, H, T, hs, dtype, lo)) return st;
+  return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, li, lo, stream);
 }
 
 int gattn_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int T,
@@ -91,14 +194,8 @@ int gattn_bwd_preprocess(const void* o, const void* dO, const float* lse, int B,
   if (!ptr_ok(o) || !ptr_ok(dO) || !ptr_ok(lse)) return GATTN_ERR_INVALID_ARG;
   if (int st = check_shape(B, H, T, hs, dtype)) return st;
   if (int st = check_workspace(workspace, workspace_bytes, B, H, T, hs, dtype)) return st;
-  float* D = ws_D(workspace);
-  float* L2 = ws_L2(workspace, B, H, T);
-  if (dtype == GATTN_F32)
-    return status_of(gattn::f32_bwd_pre(static_cast<const float*>(o), static_cast<const float*>(dO),
-                                        lse, D, L2, B * H, T, hs, stream));
-  return status_of(gattn::bf16_bwd_pre(static_cast<const uint16_t*>(o),
-                                       static_cast<const uint16_t*>(dO), lse, D, L2, B * H, T, hs,
-                                       stream));
+  return pre_impl(o, dO, lse, B, H, T, hs, dtype, workspace, gattn::contiguous_layout(H, T, hs),
+                  stream);
 }
 
 int gattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -107,22 +204,8 @@ int gattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, con
   if (!ptr_ok(o) || !ptr_ok(lse) || !ptr_ok(dq)) return GATTN_ERR_INVALID_ARG;
   if (int st = check_main(q, k, v, dO, scale, B, H, T, hs, dtype, workspace, workspace_bytes))
     return st;
-  float* D = ws_D(workspace);
-  float* L2 = ws_L2(workspace, B, H, T);
-  if (dtype == GATTN_F32) {
-    hipError_t e = gattn::f32_bwd_pre(static_cast<const float*>(o), static_cast<const float*>(dO),
-                                      lse, D, L2, B * H, T, hs, stream);
-    if (e != hipSuccess) return GATTN_ERR_HIP;
-    return status_of(gattn::f32_bwd_dq(
-        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-        static_cast<const float*>(dO), lse, D, static_cast<float*>(dq), B * H, T, hs, scale,
-        stream));
-  }
-  return status_of(gattn::bf16_bwd_dq(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
-      static_cast<const uint16_t*>(dO), lse, D, L2, static_cast<uint16_t*>(dq), B * H, T, hs,
-      scale, stream));
+  const gattn::Layout c = gattn::contiguous_layout(H, T, hs);
+  return dq_impl(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, workspace, c, c, c, stream);
 }
 
 int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk,
@@ -131,17 +214,8 @@ int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, 
   if (!ptr_ok(dk) || !ptr_ok(dv)) return GATTN_ERR_INVALID_ARG;
   if (int st = check_main(q, k, v, dO, scale, B, H, T, hs, dtype, workspace, workspace_bytes))
     return st;
-  const float* D = ws_D(workspace);
-  const float* L2 = ws_L2(workspace, B, H, T);
-  if (dtype == GATTN_F32)
-    return status_of(gattn::f32_bwd_dkdv(
-        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-        static_cast<const float*>(dO), D, L2, static_cast<float*>(dk), static_cast<float*>(dv),
-        B * H, T, hs, scale, stream));
-  return status_of(gattn::bf16_bwd_dkdv(
-      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), D, L2,
-      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B * H, T, hs, scale, stream));
+  const gattn::Layout c = gattn::contiguous_layout(H, T, hs);
+  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, c, c, c, stream);
 }
 
 int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -149,17 +223,32 @@ int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
               float scale, int dtype, void* workspace, size_t workspace_bytes,
               hipStream_t stream) {
   // Validate everything up front so that a rejected call enqueues nothing.
-  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(dO) || !ptr_ok(lse) ||
-      !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv))
-    return GATTN_ERR_INVALID_ARG;
-  if (!scale_ok(scale)) return GATTN_ERR_INVALID_ARG;
-  if (int st = check_shape(B, H, T, hs, dtype)) return st;
-  if (int st = check_workspace(workspace, workspace_bytes, B, H, T, hs, dtype)) return st;
-  int st = gattn_bwd_dq(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, workspace,
-                        workspace_bytes, stream);
-  if (st != GATTN_OK) return st;
-  return gattn_bwd_dkdv(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, workspace_bytes,
-                        stream);
+  if (int st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, T, hs, scale, dtype, workspace,
+                         workspace_bytes))
+    return st;
+  const gattn::Layout c = gattn::contiguous_layout(H, T, hs);
+  if (int st = dq_impl(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, workspace, c, c, c,
+                       stream))
+    return st;
+  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, c, c, c, stream);
+}
+
+int gattn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int T, int hs,
+                      float scale, int dtype, void* workspace, size_t workspace_bytes,
+                      const int64_t* qkv_strides, const int64_t* o_strides,
+                      const int64_t* grad_strides, hipStream_t stream) {
+  if (int st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, T, hs, scale, dtype, workspace,
+                         workspace_bytes))
+    return st;
+  gattn::Layout li, lo, lg;
+  if (int st = layout_of(qkv_strides, H, T, hs, dtype, li)) return st;
+  if (int st = layout_of(o_strides, H, T, hs, dtype, lo)) return st;
+  if (int st = layout_of(grad_strides, H, T, hs, dtype, lg)) return st;
+  if (int st = dq_impl(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, workspace, li, lo, lg,
+                       stream))
+    return st;
+  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, li, lo, lg, stream);
 }
 
 }  // extern "C"

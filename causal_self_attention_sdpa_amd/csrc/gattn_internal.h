@@ -26,6 +26,34 @@ hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t str
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, argv, 0, stream);
 }
 
+// Element strides of a (B, H, T, hs) tensor whose hs elements are contiguous:
+// element (b, h, t, d) sits at b*sb + h*sh + t*st + d.  The contiguous layout
+// is {H*T*hs, T*hs, hs}; the fused projection output (B, T, 3C) read as q (or
+// k, v at +C, +2C elements) is {T*3C, hs, 3C}; a (B, T, C) output is
+// {T*C, hs, C}.
+struct Layout {
+  int64_t sb, sh, st;
+};
+inline Layout contiguous_layout(int H, int T, int hs) {
+  return Layout{int64_t(H) * T * hs, int64_t(T) * hs, hs};
+}
+// Offset (elements) of slice (b, h) = (bh / H, bh % H).
+__host__ __device__ inline int64_t slice_offset(const Layout& l, int bh, int H) {
+  return int64_t(bh / H) * l.sb + int64_t(bh % H) * l.sh;
+}
+inline bool is_contiguous(const Layout& l, int H, int T, int hs) {
+  const Layout c = contiguous_layout(H, T, hs);
+  return l.sb == c.sb && l.sh == c.sh && l.st == c.st;
+}
+inline bool all_contiguous(int H, int T, int hs, const Layout& a, const Layout& b,
+                           const Layout& c) {
+  return is_contiguous(a, H, T, hs) && is_contiguous(b, H, T, hs) && is_contiguous(c, H, T, hs);
+}
+// Bytes spanned by one slice: rows 0 .. T-1 of hs elements of `esize` bytes.
+__host__ __device__ inline uint32_t slice_span_bytes(const Layout& l, int T, int hs, int esize) {
+  return uint32_t((int64_t(T - 1) * l.st + hs) * esize);
+}
+
 // Backward workspace: [D = rowsum(dO * O)][L2 = lse * log2(e)], each float32
 // (B, H, T) and starting on a 256-byte boundary.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -34,28 +62,33 @@ inline size_t ws_part_bytes(int B, int H, int T) {
 }
 
 // ---- float32 path (any hs <= 128, any T; wave per row; deterministic) ----
+// li: layout of q, k, v; lo: of o, dO; lg: of dq, dk, dv.  lse, D and L2 are
+// contiguous (B, H, T).
 hipError_t f32_fwd(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
-                   int T, int hs, float scale, hipStream_t s);
+                   int H, int T, int hs, float scale, Layout li, Layout lo, hipStream_t s);
 hipError_t f32_bwd_pre(const float* o, const float* dO, const float* lse, float* D, float* L2,
-                       int BH, int T, int hs, hipStream_t s);
+                       int BH, int H, int T, int hs, Layout lo, hipStream_t s);
 hipError_t f32_bwd_dkdv(const float* q, const float* k, const float* v, const float* dO,
-                        const float* D, const float* L2, float* dk, float* dv, int BH, int T,
-                        int hs, float scale, hipStream_t s);
+                        const float* D, const float* L2, float* dk, float* dv, int BH, int H,
+                        int T, int hs, float scale, Layout li, Layout lo, Layout lg,
+                        hipStream_t s);
 hipError_t f32_bwd_dq(const float* q, const float* k, const float* v, const float* dO,
-                      const float* lse, const float* D, float* dq, int BH, int T, int hs,
-                      float scale, hipStream_t s);
+                      const float* lse, const float* D, float* dq, int BH, int H, int T, int hs,
+                      float scale, Layout li, Layout lo, Layout lg, hipStream_t s);
 
 // ---- bf16 path (hs in {32, 64}; MFMA) ----
 hipError_t bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                    float* lse, int BH, int T, int hs, float scale, hipStream_t s);
+                    float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
+                    hipStream_t s);
 hipError_t bf16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                        float* L2, int BH, int T, int hs, hipStream_t s);
+                        float* L2, int BH, int H, int T, int hs, Layout lo, hipStream_t s);
 hipError_t bf16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
-                         uint16_t* dv, int BH, int T, int hs, float scale, hipStream_t s);
+                         uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
+                         Layout lo, Layout lg, hipStream_t s);
 hipError_t bf16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                       float* L2, uint16_t* dq, int BH, int T, int hs, float scale,
-                       hipStream_t s);
+                       float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
+                       Layout li, Layout lo, Layout lg, hipStream_t s);
 
 }  // namespace gattn

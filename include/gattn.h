@@ -20,8 +20,11 @@
  *   dV[j] = sum_{i>=j} P[i][j] dO[i],  dQ[i] = scale * sum_{j<=i} dS[i][j] K[j],
  *   dK[j] = scale * sum_{i>=j} dS[i][j] Q[i].
  *
- * Layout: every tensor is contiguous (B, H, T, hs), row-major, hs innermost;
- * lse and D are contiguous (B, H, T) float32.  The T x T mask is never
+ * Layout: the plain entry points take every tensor contiguous (B, H, T, hs),
+ * row-major, hs innermost; the *_strided entry points take element strides
+ * {batch, head, row} for each group of tensors (hs always contiguous), so the
+ * fused projection output (B, T, 3C) and a (B, T, C) output are used in place.
+ * lse and D are always contiguous (B, H, T) float32.  The T x T mask is never
  * materialised.
  *
  * Dtypes: q, k, v, o, dO, dq, dk, dv all have `dtype`; lse is always float32.
@@ -51,6 +54,7 @@
 #define GATTN_H
 
 #include <stddef.h>
+#include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -82,6 +86,25 @@ int gattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int H, int T, int hs, float scale, int dtype, hipStream_t stream);
 
 /*
+ * Forward on strided tensors: as gattn_fwd, with element (b, h, t, d) of q, k
+ * and v at b*s[0] + h*s[1] + t*s[2] + d for s = qkv_strides (one stride set
+ * shared by q, k and v, each from its own base pointer), and of o for
+ * s = o_strides; lse stays contiguous (B, H, T).  A NULL stride pointer means
+ * the contiguous layout {H*T*hs, T*hs, hs}.  Example, the attention of a GPT
+ * block with C = H*hs: qkv_strides = {T*3C, hs, 3C} with q = qkv, k = qkv + C,
+ * v = qkv + 2C (elements) reads the (B, T, 3C) output of the fused projection
+ * directly, and o_strides = {T*C, hs, C} writes o as (B, T, C).
+ * Extra INVALID_ARG cases: a stride < 0, a row stride < hs (rows overlap), a
+ * stride whose byte size is not a multiple of 16, or (T + 256) rows of one
+ * slice spanning 2^31 bytes or more.  The caller is responsible for o not
+ * overlapping itself across heads or batches (any layout of distinct rows is
+ * accepted) and for o not aliasing q, k or v.
+ */
+int gattn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int T, int hs, float scale, int dtype,
+                      const int64_t* qkv_strides, const int64_t* o_strides, hipStream_t stream);
+
+/*
  * Bytes of device workspace the backward needs: D = rowsum(dO * o) and
  * lse * log2(e), each float32 (B, H, T) starting on a 256-byte boundary.
  * Returns 0 for arguments gattn_bwd would reject.
@@ -104,6 +127,22 @@ int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
               const float* lse, void* dq, void* dk, void* dv,
               int B, int H, int T, int hs, float scale, int dtype,
               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward on strided tensors: as gattn_bwd, with q, k, v addressed by
+ * qkv_strides, o and dO by o_strides, and dq, dk, dv by grad_strides (same
+ * convention and checks as gattn_fwd_strided; NULL = contiguous).  For a GPT
+ * block: o_strides = {T*C, hs, C} reads o and the incoming gradient dO as
+ * (B, T, C), and grad_strides = {T*3C, hs, 3C} with dq = dqkv, dk = dqkv + C,
+ * dv = dqkv + 2C writes the gradient of the fused projection output directly.
+ * The workspace is the same as gattn_bwd's.
+ */
+int gattn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int H, int T, int hs, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, const int64_t* qkv_strides,
+                      const int64_t* o_strides, const int64_t* grad_strides,
+                      hipStream_t stream);
 
 /*
  * Backward, row terms only: D[i] = sum_d dO[i][d] * o[i][d] (the row term of

@@ -122,3 +122,59 @@ def test_stage_validation(lib):
     assert lib.gattn_bwd_dkdv(*([P] * 6), 1, 1, 8, 64, 0.125, 1, P, 4, None) == WORKSPACE
     assert lib.gattn_bwd_dkdv(*([P] * 6), 1, 1, 8, 64, 0.125, 1, P + 64, 1 << 20,
                               None) == WORKSPACE
+
+
+def _st(*s):
+    return (ctypes.c_int64 * 3)(*s)
+
+
+def test_fwd_strided_validation(lib):
+    B, H, T, hs = 2, 3, 8, 64
+    good = _st(T * 3 * H * hs, hs, 3 * H * hs)  # fused (B, T, 3C) projection output
+
+    def f(qkv=good, o=None, dtype=1, **kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=P, B=B, H=H, T=T, hs=hs, scale=0.125)
+        a.update(kw)
+        return lib.gattn_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                     a["T"], a["hs"], a["scale"], dtype, qkv, o, None)
+
+    # the checks shared with gattn_fwd
+    assert f(q=None) == INVALID
+    assert f(v=P + 2) == INVALID
+    assert f(scale=-1.0) == INVALID
+    assert f(hs=48) == UNSUPPORTED
+    # stride checks: negative, overlapping rows, rows off 16-byte boundaries, span
+    assert f(qkv=_st(-8, hs, 3 * H * hs)) == INVALID
+    assert f(qkv=_st(T * 3 * H * hs, -hs, 3 * H * hs)) == INVALID
+    assert f(qkv=_st(T * 3 * H * hs, hs, hs - 8)) == INVALID   # row stride < hs
+    assert f(qkv=_st(T * 3 * H * hs, hs, 3 * H * hs + 4)) == INVALID  # 8-byte rows
+    assert f(o=_st(4, hs, H * hs)) == INVALID                  # batch stride of 8 bytes
+    assert f(o=_st(T * H * hs, 12, H * hs)) == INVALID         # head stride of 24 bytes
+    assert f(qkv=_st(0, 0, 1 << 22), T=1 << 8) == INVALID       # (T + 256) rows >= 2^31 bytes
+    assert f(qkv=_st(0, 0, 1 << 20), T=1 << 8, dtype=0) == INVALID  # same for float32
+    # float32 strides count 4-byte elements: 4 elements = 16 bytes is fine for
+    # alignment, but not below hs
+    assert f(qkv=_st(4, 4, 4), hs=8, dtype=0) == INVALID
+
+
+def test_bwd_strided_validation(lib):
+    B, H, T, hs = 2, 3, 8, 64
+    qkv = _st(T * 3 * H * hs, hs, 3 * H * hs)
+    out = _st(T * H * hs, hs, H * hs)
+
+    def f(ptrs=None, s_qkv=qkv, s_o=out, s_g=qkv, ws=P, wsb=1 << 20, **kw):
+        p = ptrs or [P] * 9
+        a = dict(B=B, H=H, T=T, hs=hs, scale=0.125, dtype=1)
+        a.update(kw)
+        return lib.gattn_bwd_strided(*p, a["B"], a["H"], a["T"], a["hs"], a["scale"], a["dtype"],
+                                     ws, wsb, s_qkv, s_o, s_g, None)
+
+    for i in range(9):
+        p = [P] * 9
+        p[i] = None
+        assert f(p) == INVALID, i
+    assert f(ws=None) == WORKSPACE
+    assert f(wsb=16) == WORKSPACE
+    assert f(s_o=_st(T * H * hs, hs, hs - 1)) == INVALID
+    assert f(s_g=_st(T * H * hs, hs + 1, H * hs)) == INVALID
+    assert f(s_qkv=_st(-1, hs, 3 * H * hs)) == INVALID
