@@ -34,6 +34,7 @@ at the run's clocks, next to the published peaks.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -195,6 +196,12 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2-124m")
+    ap.add_argument("--layout", choices=("contiguous", "fused", "copies"), default="contiguous",
+                    help="contiguous: (B,H,T,hs) tensors (the metric); fused: q, k, v read in "
+                         "place from a GPT block's (B,T,3C) projection output, y and dy (B,T,C), "
+                         "dqkv (B,T,3C), through the strided entry points; copies: the "
+                         "contiguous kernels plus the transposes a caller of the contiguous "
+                         "entry points needs around them")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-slices", type=int, default=400,
@@ -284,7 +291,69 @@ def main() -> int:
         if st != 0:
             raise RuntimeError(f"{name} failed with status {st}")
 
+    if args.layout != "contiguous":
+        C = H * hs
+        st = lambda *v: (ctypes.c_int64 * 3)(*v)
+        s_qkv, s_bc = st(T * 3 * C, hs, 3 * C), st(T * C, hs, C)
+        to_btc = lambda a: a.transpose(1, 2).reshape(B, T, C)
+        for t in layers:
+            t["qkv"] = torch.cat([to_btc(t[n]) for n in ("q", "k", "v")], dim=2).contiguous()
+            t["dy"] = to_btc(t["do"]).contiguous()
+            t["y"] = torch.empty((B, T, C), dtype=torch.bfloat16, device=dev)
+            t["dqkv"] = torch.empty_like(t["qkv"])
+            for n in ("q", "k", "v", "do", "o", "dq", "dk", "dv"):
+                t[n] = None if args.layout == "fused" else t[n]
+        eb = 2  # bytes per element
+
+        def fwd_fused(t):
+            a = t["qkv"].data_ptr()
+            return lib.gattn_fwd_strided(a, a + C * eb, a + 2 * C * eb, p(t["y"]), p(t["lse"]),
+                                         B, H, T, hs, scale, ga.BF16, s_qkv, s_bc, sp)
+
+        def bwd_fused(t):
+            a, g = t["qkv"].data_ptr(), t["dqkv"].data_ptr()
+            return lib.gattn_bwd_strided(a, a + C * eb, a + 2 * C * eb, p(t["y"]), p(t["dy"]),
+                                         p(t["lse"]), g, g + C * eb, g + 2 * C * eb, B, H, T, hs,
+                                         scale, ga.BF16, p(ws), wsb, s_qkv, s_bc, s_qkv, sp)
+
+        def fwd_copies(t):
+            # what a caller of the contiguous entry points does around them
+            qkv = t["qkv"].view(B, T, 3, H, hs).permute(2, 0, 3, 1, 4).contiguous()
+            t["q"], t["k"], t["v"] = qkv[0], qkv[1], qkv[2]
+            r = lib.gattn_fwd(p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["lse"]), B, H, T,
+                              hs, scale, ga.BF16, sp)
+            t["y"].copy_(to_btc(t["o"]))
+            return r
+
+        def bwd_copies(t):
+            t["do"] = t["dy"].view(B, T, H, hs).transpose(1, 2).contiguous()
+            r = lib.gattn_bwd(p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["do"]),
+                              p(t["lse"]), p(t["dq"]), p(t["dk"]), p(t["dv"]), B, H, T, hs,
+                              scale, ga.BF16, p(ws), wsb, sp)
+            t["dqkv"].copy_(torch.stack((t["dq"], t["dk"], t["dv"]), dim=2)
+                            .permute(0, 3, 2, 1, 4).reshape(B, T, 3 * C))
+            return r
+
+        fwd_l, bwd_l = (fwd_fused, bwd_fused) if args.layout == "fused" else (fwd_copies,
+                                                                             bwd_copies)
+
+    def step_layout(record: int | None):
+        if record is not None:
+            timer.record(seq[record][0], sp)
+        for l in range(L):
+            if fwd_l(layers[l]) != 0:
+                raise RuntimeError("forward failed")
+        if record is not None:
+            timer.record(seq[record][1], sp)
+        for l in reversed(range(L)):
+            if bwd_l(layers[l]) != 0:
+                raise RuntimeError("backward failed")
+        if record is not None:
+            timer.record(seq[record][2], sp)
+
     def step(record: int | None):
+        if args.layout != "contiguous":
+            return step_layout(record)
         # record = index of a timed step: its events bracket the kernels of layer record % L
         lt = None if record is None else record % L
         if record is not None:
@@ -319,6 +388,22 @@ def main() -> int:
     fwd_ms = [timer.elapsed_ms(a, b) for a, b, _ in seq]
     bwd_ms = [timer.elapsed_ms(b, c) for _, b, c in seq]
     pairs = B * H * T * (T + 1) // 2
+    if args.layout != "contiguous":
+        out = {"metric": metric, "value": round(value, 3), "unit": "TFLOP/s",
+               "pct_of_bf16_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 3), "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "data": "synthetic",
+               "config": {"workload": W["label"], "layout": args.layout, "B": B, "H": H, "T": T,
+                          "hs": hs, "layers": L, "qkv_scale": W["qkv_scale"],
+                          "parallelism": "single GPU"},
+               "fwd_ms": {"median": round(float(np.median(fwd_ms)), 4),
+                          "min": round(min(fwd_ms), 4)},
+               "bwd_ms": {"median": round(float(np.median(bwd_ms)), 4),
+                          "min": round(min(bwd_ms), 4)},
+               "roofline": None}
+        print(json.dumps(out), flush=True)
+        return 0
     mean_us = {k: float(np.mean([timer.elapsed_ms(a, b) for a, b in ev[k]])) * 1e3
                for k in KERNELS}
     dom = max(mean_us, key=mean_us.get)
