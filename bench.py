@@ -68,9 +68,9 @@ CSRC = os.path.join(ROOT, "causal_self_attention_sdpa_amd", "csrc")
 #          algorithmic bytes per launch in units of one (B,H,T,hs) bf16 tensor, and of one
 #          (B,H,T) fp32 row vector)
 KERNELS = {
-    "fwd": ("bf16_fwd_kernel<{hs}, false>", "bf16_fwd.hip", 4, 4, 1),   # q k v in, o, lse out
-    "dq": ("bf16_dq_kernel<{hs}, false>", "bf16_bwd.hip", 2, 6, 1),  # q k v o dO lse in, dq out
-    "dkdv": ("bf16_dkdv_kernel<{hs}, false>", "bf16_bwd.hip", 6, 6, 0),  # q k v dO in, dk dv out
+    "fwd": ("fwd16_kernel<{E}, {hs}, false>", "mfma16_fwd.hip", 4, 4, 1),  # q k v in; o, lse out
+    "dq": ("dq16_kernel<{E}, {hs}, false>", "mfma16_bwd.hip", 2, 6, 1),  # q k v o dO lse in; dq out
+    "dkdv": ("dkdv16_kernel<{E}, {hs}, false>", "mfma16_bwd.hip", 6, 6, 0),  # q k v dO in; dk dv out
 }
 
 
@@ -196,6 +196,8 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2-124m")
+    ap.add_argument("--dtype", choices=("bf16", "f16"), default="bf16",
+                    help="16-bit storage type of q, k, v, o and the gradients")
     ap.add_argument("--layout", choices=("contiguous", "fused", "copies"), default="contiguous",
                     help="contiguous: (B,H,T,hs) tensors (the metric); fused: q, k, v read in "
                          "place from a GPT block's (B,T,3C) projection output, y and dy (B,T,C), "
@@ -235,6 +237,8 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n}))
         return 0
 
+    tdt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
+    dcode = ga.BF16 if args.dtype == "bf16" else ga.F16
     W = WORKLOADS[args.workload]
     B, H, T, hs, L = W["B"], W["H"], W["T"], W["hs"], W["layers"]
     tag = f"b{B}h{H}t{T}"
@@ -245,17 +249,18 @@ def main() -> int:
     layers = []
     host = []  # host copies of the layers the CPU baseline samples
     for l in range(L):
-        x = si.attention_inputs(B, H, T, hs, "bf16", seed=2024, workload=f"{args.workload}-attn",
-                                layer=l, qkv_scale=W["qkv_scale"])
+        x = si.attention_inputs(B, H, T, hs, args.dtype, seed=2024,
+                                workload=f"{args.workload}-attn", layer=l,
+                                qkv_scale=W["qkv_scale"])
         if l * B * H < args.cpu_slices:
             host.append(x)
-        t = {n: torch.from_numpy(a).to(dev).to(torch.bfloat16) for n, a in x.items()}
+        t = {n: torch.from_numpy(a).to(dev).to(tdt) for n, a in x.items()}
         t["o"] = torch.empty_like(t["q"])
         t["lse"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
         for g in ("dq", "dk", "dv"):
             t[g] = torch.empty_like(t["q"])
         layers.append(t)
-    ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16), dtype=torch.uint8,
+    ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, dcode), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream()
     timer = HipTimer()
@@ -272,12 +277,12 @@ def main() -> int:
     for t in layers:
         call.append({
             "fwd": (lib.gattn_fwd, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["lse"]),
-                                    B, H, T, hs, scale, ga.BF16, sp)),
+                                    B, H, T, hs, scale, dcode, sp)),
             "dq": (lib.gattn_bwd_dq, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["do"]),
-                                      p(t["lse"]), p(t["dq"]), B, H, T, hs, scale, ga.BF16, p(ws),
+                                      p(t["lse"]), p(t["dq"]), B, H, T, hs, scale, dcode, p(ws),
                                       wsb, sp)),
             "dkdv": (lib.gattn_bwd_dkdv, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["do"]),
-                                          p(t["dk"]), p(t["dv"]), B, H, T, hs, scale, ga.BF16,
+                                          p(t["dk"]), p(t["dv"]), B, H, T, hs, scale, dcode,
                                           p(ws), wsb, sp)),
         })
 
@@ -299,7 +304,7 @@ def main() -> int:
         for t in layers:
             t["qkv"] = torch.cat([to_btc(t[n]) for n in ("q", "k", "v")], dim=2).contiguous()
             t["dy"] = to_btc(t["do"]).contiguous()
-            t["y"] = torch.empty((B, T, C), dtype=torch.bfloat16, device=dev)
+            t["y"] = torch.empty((B, T, C), dtype=tdt, device=dev)
             t["dqkv"] = torch.empty_like(t["qkv"])
             for n in ("q", "k", "v", "do", "o", "dq", "dk", "dv"):
                 t[n] = None if args.layout == "fused" else t[n]
@@ -308,20 +313,20 @@ def main() -> int:
         def fwd_fused(t):
             a = t["qkv"].data_ptr()
             return lib.gattn_fwd_strided(a, a + C * eb, a + 2 * C * eb, p(t["y"]), p(t["lse"]),
-                                         B, H, T, hs, scale, ga.BF16, s_qkv, s_bc, sp)
+                                         B, H, T, hs, scale, dcode, s_qkv, s_bc, sp)
 
         def bwd_fused(t):
             a, g = t["qkv"].data_ptr(), t["dqkv"].data_ptr()
             return lib.gattn_bwd_strided(a, a + C * eb, a + 2 * C * eb, p(t["y"]), p(t["dy"]),
                                          p(t["lse"]), g, g + C * eb, g + 2 * C * eb, B, H, T, hs,
-                                         scale, ga.BF16, p(ws), wsb, s_qkv, s_bc, s_qkv, sp)
+                                         scale, dcode, p(ws), wsb, s_qkv, s_bc, s_qkv, sp)
 
         def fwd_copies(t):
             # what a caller of the contiguous entry points does around them
             qkv = t["qkv"].view(B, T, 3, H, hs).permute(2, 0, 3, 1, 4).contiguous()
             t["q"], t["k"], t["v"] = qkv[0], qkv[1], qkv[2]
             r = lib.gattn_fwd(p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["lse"]), B, H, T,
-                              hs, scale, ga.BF16, sp)
+                              hs, scale, dcode, sp)
             t["y"].copy_(to_btc(t["o"]))
             return r
 
@@ -329,7 +334,7 @@ def main() -> int:
             t["do"] = t["dy"].view(B, T, H, hs).transpose(1, 2).contiguous()
             r = lib.gattn_bwd(p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["do"]),
                               p(t["lse"]), p(t["dq"]), p(t["dk"]), p(t["dv"]), B, H, T, hs,
-                              scale, ga.BF16, p(ws), wsb, sp)
+                              scale, dcode, p(ws), wsb, sp)
             t["dqkv"].copy_(torch.stack((t["dq"], t["dk"], t["dv"]), dim=2)
                             .permute(0, 3, 2, 1, 4).reshape(B, T, 3 * C))
             return r
@@ -392,7 +397,7 @@ def main() -> int:
         out = {"metric": metric, "value": round(value, 3), "unit": "TFLOP/s",
                "pct_of_bf16_peak": round(100.0 * value / MFMA_BF16_PEAK_TFLOPS, 3), "n_gpus": 1,
                "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": args.dtype,
                "data": "synthetic",
                "config": {"workload": W["label"], "layout": args.layout, "B": B, "H": H, "T": T,
                           "hs": hs, "layers": L, "qkv_scale": W["qkv_scale"],
@@ -407,7 +412,7 @@ def main() -> int:
     mean_us = {k: float(np.mean([timer.elapsed_ms(a, b) for a, b in ev[k]])) * 1e3
                for k in KERNELS}
     dom = max(mean_us, key=mean_us.get)
-    sym = KERNELS[dom][0].format(hs=hs)
+    sym = KERNELS[dom][0].format(hs=hs, E="Bf16" if args.dtype == "bf16" else "F16")
     if W["bound"] == "mfma":
         alg = KERNELS[dom][2] * hs * pairs
         achieved = alg / (mean_us[dom] * 1e-6) / 1e12
@@ -434,7 +439,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {"workload": W["label"],
                    "B": B, "H": H, "T": T, "hs": hs, "layers": L, "qkv_scale": W["qkv_scale"],

@@ -15,6 +15,7 @@ gradient dqkv (B, T, 3C) through the strided entry points.
 """
 from ._binding import (  # noqa: F401
     BF16,
+    F16,
     F32,
     GattnError,
     attention_backward,

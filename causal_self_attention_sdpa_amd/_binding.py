@@ -10,6 +10,7 @@ _LIB_PATH = os.path.join(PKG, "libgattn.so")
 
 F32 = 0
 BF16 = 1
+F16 = 2
 _STATUS = {0: "GATTN_OK", 1: "GATTN_ERR_INVALID_ARG", 2: "GATTN_ERR_UNSUPPORTED",
            3: "GATTN_ERR_WORKSPACE", 4: "GATTN_ERR_HIP"}
 
@@ -78,6 +79,8 @@ def _dtype_code(t) -> int:
         return BF16
     if t.dtype == torch.float32:
         return F32
+    if t.dtype == torch.float16:
+        return F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 

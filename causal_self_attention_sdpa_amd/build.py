@@ -34,8 +34,8 @@ FLAGS = [
 # lets the compiler fold the row maxima into v_max3_f32 instead of quieting
 # every MFMA result first.  The float32 path keeps full IEEE semantics.
 FILE_FLAGS = {
-    "bf16_fwd.hip": ["-fno-honor-nans"],
-    "bf16_bwd.hip": ["-fno-honor-nans"],
+    "mfma16_fwd.hip": ["-fno-honor-nans"],
+    "mfma16_bwd.hip": ["-fno-honor-nans"],
 }
 
 

@@ -1,5 +1,5 @@
 // C-ABI entry points of libgattn: argument validation (before any HIP call)
-// and dispatch to the float32 or bf16 kernels.  Semantics and error codes are
+// and dispatch to the float32 or 16-bit (bf16, fp16) kernels.  Semantics and error codes are
 // documented in include/gattn.h.
 #include "gattn.h"
 
@@ -17,9 +17,9 @@ bool ptr_ok(const void* p) { return p != nullptr && aligned(p, 16); }
 
 int check_shape(int B, int H, int T, int hs, int dtype) {
   if (B < 1 || H < 1 || T < 1 || hs < 1) return GATTN_ERR_INVALID_ARG;
-  if (dtype != GATTN_F32 && dtype != GATTN_BF16) return GATTN_ERR_INVALID_ARG;
+  if (dtype != GATTN_F32 && dtype != GATTN_BF16 && dtype != GATTN_F16) return GATTN_ERR_INVALID_ARG;
   if (int64_t(B) * H * T * hs >= (int64_t(1) << 31)) return GATTN_ERR_INVALID_ARG;
-  if (dtype == GATTN_BF16 && hs != 32 && hs != 64) return GATTN_ERR_UNSUPPORTED;
+  if (dtype != GATTN_F32 && hs != 32 && hs != 64) return GATTN_ERR_UNSUPPORTED;
   if (dtype == GATTN_F32 && hs > 128) return GATTN_ERR_UNSUPPORTED;
   return GATTN_OK;
 }
@@ -78,9 +78,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
     return status_of(gattn::f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
                                     static_cast<const float*>(v), static_cast<float*>(o), lse, BH,
                                     H, T, hs, scale, li, lo, stream));
-  return status_of(gattn::bf16_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                   static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
-                                   BH, H, T, hs, scale, li, lo, stream));
+  return status_of(gattn::h16_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                  static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
+                                  BH, H, T, hs, scale, li, lo, dtype == GATTN_F16, stream));
 }
 
 int pre_impl(const void* o, const void* dO, const float* lse, int B, int H, int T, int hs,
@@ -90,9 +90,9 @@ int pre_impl(const void* o, const void* dO, const float* lse, int B, int H, int 
   if (dtype == GATTN_F32)
     return status_of(gattn::f32_bwd_pre(static_cast<const float*>(o), static_cast<const float*>(dO),
                                         lse, D, L2, B * H, H, T, hs, lo, stream));
-  return status_of(gattn::bf16_bwd_pre(static_cast<const uint16_t*>(o),
-                                       static_cast<const uint16_t*>(dO), lse, D, L2, B * H, H, T,
-                                       hs, lo, stream));
+  return status_of(gattn::h16_bwd_pre(static_cast<const uint16_t*>(o),
+                                      static_cast<const uint16_t*>(dO), lse, D, L2, B * H, H, T,
+                                      hs, lo, dtype == GATTN_F16, stream));
 }
 
 int dq_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -108,11 +108,11 @@ int dq_impl(const void* q, const void* k, const void* v, const void* o, const vo
         static_cast<const float*>(dO), lse, D, static_cast<float*>(dq), B * H, H, T, hs, scale, li,
         lo, lg, stream));
   }
-  return status_of(gattn::bf16_bwd_dq(
+  return status_of(gattn::h16_bwd_dq(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
       static_cast<const uint16_t*>(dO), lse, D, L2, static_cast<uint16_t*>(dq), B * H, H, T, hs,
-      scale, li, lo, lg, stream));
+      scale, li, lo, lg, dtype == GATTN_F16, stream));
 }
 
 int dkdv_impl(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
@@ -125,11 +125,11 @@ int dkdv_impl(const void* q, const void* k, const void* v, const void* dO, void*
         static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
         static_cast<const float*>(dO), D, L2, static_cast<float*>(dk), static_cast<float*>(dv),
         B * H, H, T, hs, scale, li, lo, lg, stream));
-  return status_of(gattn::bf16_bwd_dkdv(
+  return status_of(gattn::h16_bwd_dkdv(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), D, L2,
       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B * H, H, T, hs, scale, li, lo, lg,
-      stream));
+      dtype == GATTN_F16, stream));
 }
 
 int check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

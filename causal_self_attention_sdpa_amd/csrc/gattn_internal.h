@@ -76,19 +76,20 @@ hipError_t f32_bwd_dq(const float* q, const float* k, const float* v, const floa
                       const float* lse, const float* D, float* dq, int BH, int H, int T, int hs,
                       float scale, Layout li, Layout lo, Layout lg, hipStream_t s);
 
-// ---- bf16 path (hs in {32, 64}; MFMA) ----
-hipError_t bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                    float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
-                    hipStream_t s);
-hipError_t bf16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                        float* L2, int BH, int H, int T, int hs, Layout lo, hipStream_t s);
-hipError_t bf16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
-                         uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
-                         Layout lo, Layout lg, hipStream_t s);
-hipError_t bf16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                       const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                       float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
-                       Layout li, Layout lo, Layout lg, hipStream_t s);
+// ---- 16-bit path: bf16 (f16 = false) or fp16 (f16 = true), hs in {32, 64}; MFMA ----
+hipError_t h16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                   float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
+                   bool f16, hipStream_t s);
+hipError_t h16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
+                       float* L2, int BH, int H, int T, int hs, Layout lo, bool f16,
+                       hipStream_t s);
+hipError_t h16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
+                        uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
+                        Layout lo, Layout lg, bool f16, hipStream_t s);
+hipError_t h16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
+                      float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
+                      Layout li, Layout lo, Layout lg, bool f16, hipStream_t s);
 
 }  // namespace gattn

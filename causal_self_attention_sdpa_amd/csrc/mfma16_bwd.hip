@@ -1,4 +1,5 @@
-// bf16 causal attention backward on gfx950 MFMA: two main kernels, no atomics.
+// 16-bit (bf16 or fp16) causal attention backward on gfx950 MFMA: two main
+// kernels, no atomics; E is the element type's traits.
 //
 // The pages state only that the model is trained with a backward pass; the
 // gradients are the chain rule of the forward ("Let's build GPT" summary
@@ -26,7 +27,7 @@
 // its P is 1, but its dP, dS and dO are 0, so it adds exactly nothing.
 #include <cmath>
 
-#include "bf16_common.h"
+#include "mfma16_common.h"
 #include "gattn_internal.h"
 
 #ifndef GATTN_DKDV_STAGES
@@ -50,8 +51,8 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------
 // D[i] = sum_d dO[i][d] * O[i][d] and L2[i] = lse[i] * log2(e); HS/8 threads
 // per row, 16-byte loads.
-template <int HS>
-__global__ __launch_bounds__(kThreads) void bf16_pre_kernel(const uint16_t* __restrict__ o,
+template <class E, int HS>
+__global__ __launch_bounds__(kThreads) void pre16_kernel(const uint16_t* __restrict__ o,
                                                            const uint16_t* __restrict__ dO,
                                                            const float* __restrict__ lse,
                                                            float* __restrict__ D,
@@ -69,8 +70,8 @@ __global__ __launch_bounds__(kThreads) void bf16_pre_kernel(const uint16_t* __re
     const u32x4 b = *reinterpret_cast<const u32x4*>(dO + off);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      s = fmaf(bf16lo(a[w]), bf16lo(b[w]), s);
-      s = fmaf(bf16hi(a[w]), bf16hi(b[w]), s);
+      s = fmaf(E::lo(a[w]), E::lo(b[w]), s);
+      s = fmaf(E::hi(a[w]), E::hi(b[w]), s);
     }
   }
 #pragma unroll
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void bf16_pre_kernel(const uint16_t* __re
 //   A(b): S = Q K^T, dP = dO V^T    C[query][key]; Q, dO rows read from LDS in
 //                                   perm_row order, so each lane's registers
 //                                   8t..8t+7 are 8 consecutive queries
-//   B(b): P, dS (f32, registers) -> bf16, exactly the B operand of
+//   B(b): P, dS (f32, registers) -> 16-bit, exactly the B operand of
 //   C(b): dV^T += dO^T P, dK^T += Q^T dS   C[d][key]; dO^T, Q^T via LDS
 //                                          transpose reads
 // In the steps that meet the diagonal, blocks wholly before this wavefront's
@@ -116,7 +117,7 @@ struct DkdvRegs {
 };
 
 // A(b): S and dP of query block qb.
-template <int HS>
+template <class E, int HS>
 __device__ inline void dkdv_sdp(const uint16_t* Qb, const uint16_t* Gb, int qb,
                                 const LaneOffsets<HS>& L, const DkdvRegs<HS>& R, f32x16& s,
                                 f32x16& dp) {
@@ -125,13 +126,13 @@ __device__ inline void dkdv_sdp(const uint16_t* Qb, const uint16_t* Gb, int qb,
   dp = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < C::KSTEP; ++ks) {
-    s = mfma32(op_nat<HS>(Qb, L, qb * 32, ks), R.kf[ks], s);
-    dp = mfma32(op_nat<HS>(Gb, L, qb * 32, ks), R.vf[ks], dp);
+    s = E::mfma(op_nat<HS>(Qb, L, qb * 32, ks), R.kf[ks], s);
+    dp = E::mfma(op_nat<HS>(Gb, L, qb * 32, ks), R.vf[ks], dp);
   }
 }
 
 // B(b) then C(b) for query block qb.
-template <int HS, bool MASK>
+template <class E, int HS, bool MASK>
 __device__ inline void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
                                  const float* Db, int qb, int qs0, int krow, int h, float c,
                                  const LaneOffsets<HS>& L, const f32x16& s, const f32x16& dp,
@@ -157,8 +158,8 @@ __device__ inline void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const f
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      pp[t][e] = pack_bf16(pv[2 * e], pv[2 * e + 1]);
-      dsp[t][e] = pack_bf16(dsv[2 * e], dsv[2 * e + 1]);
+      pp[t][e] = E::pack(pv[2 * e], pv[2 * e + 1]);
+      dsp[t][e] = E::pack(dsv[2 * e], dsv[2 * e + 1]);
     }
   }
 #pragma unroll
@@ -166,13 +167,13 @@ __device__ inline void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const f
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
       const int k0 = qb * 32 + 16 * t;
-      R.dva[db] = mfma32(op_tr<HS>(Gb, L, k0, db), pp[t], R.dva[db]);
-      R.dka[db] = mfma32(op_tr<HS>(Qb, L, k0, db), dsp[t], R.dka[db]);
+      R.dva[db] = E::mfma(op_tr<HS>(Gb, L, k0, db), pp[t], R.dva[db]);
+      R.dka[db] = E::mfma(op_tr<HS>(Qb, L, k0, db), dsp[t], R.dka[db]);
     }
 }
 
 // One step below the diagonal: every block is visible, no mask.
-template <int HS>
+template <class E, int HS>
 __device__ inline void dkdv_step_full(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
                                       const float* Db, int qs0, int krow, int h, float c,
                                       const LaneOffsets<HS>& L, DkdvRegs<HS>& R) {
@@ -180,14 +181,14 @@ __device__ inline void dkdv_step_full(const uint16_t* Qb, const uint16_t* Gb, co
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     f32x16 s, dp;
-    dkdv_sdp<HS>(Qb, Gb, qb, L, R, s, dp);
-    dkdv_grad<HS, false>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R);
+    dkdv_sdp<E, HS>(Qb, Gb, qb, L, R, s, dp);
+    dkdv_grad<E, HS, false>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R);
   }
 }
 
 // A step that meets the diagonal: blocks wholly before this wavefront's keys
 // are skipped, the others masked.
-template <int HS>
+template <class E, int HS>
 __device__ inline void dkdv_step_diag(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
                                       const float* Db, int qs0, int kw0, int krow, int h, float c,
                                       const LaneOffsets<HS>& L, DkdvRegs<HS>& R) {
@@ -196,16 +197,16 @@ __device__ inline void dkdv_step_diag(const uint16_t* Qb, const uint16_t* Gb, co
   for (int qb = 0; qb < C::QB; ++qb) {
     if (kw0 > qs0 + qb * 32 + 31) continue;  // all of this wavefront's keys lie after the block
     f32x16 s, dp;
-    dkdv_sdp<HS>(Qb, Gb, qb, L, R, s, dp);
-    dkdv_grad<HS, true>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R);
+    dkdv_sdp<E, HS>(Qb, Gb, qb, L, R, s, dp);
+    dkdv_grad<E, HS, true>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R);
   }
 }
 
 // STRIDED = false: every tensor is contiguous (B, H, T, hs) and the row
 // strides are the compile-time HS (the strides' registers and multiplies
 // would otherwise push this kernel into spills).
-template <int HS, bool STRIDED>
-__global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void bf16_dkdv_kernel(
+template <class E, int HS, bool STRIDED>
+__global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void dkdv16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
     const float* __restrict__ Dg, const float* __restrict__ L2g, uint16_t* __restrict__ dk,
@@ -272,9 +273,9 @@ __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void bf16_dkdv_kernel(
     if (t + C::NS - 1 < nsteps) issue(qt0 + t + C::NS - 1, (buf + C::NS - 1) % C::NS);
     const int qs0 = (qt0 + t) * C::BQ;
     if (qs0 < k0 + C::BN)
-      dkdv_step_diag<HS>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, kw0, krow, h, c, L, R);
+      dkdv_step_diag<E, HS>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, kw0, krow, h, c, L, R);
     else
-      dkdv_step_full<HS>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, krow, h, c, L, R);
+      dkdv_step_full<E, HS>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, krow, h, c, L, R);
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nsteps - t - 2)));
     __syncthreads();
   };
@@ -290,10 +291,10 @@ __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void bf16_dkdv_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t off = uint32_t(krow * rsg + db * 32 + 8 * g + 4 * h) * 2;
-      bstore8(wv, off, u32x2{pack_bf16(R.dva[db][4 * g], R.dva[db][4 * g + 1]),
-                             pack_bf16(R.dva[db][4 * g + 2], R.dva[db][4 * g + 3])});
-      bstore8(wk, off, u32x2{pack_bf16(R.dka[db][4 * g] * scale, R.dka[db][4 * g + 1] * scale),
-                             pack_bf16(R.dka[db][4 * g + 2] * scale, R.dka[db][4 * g + 3] * scale)});
+      bstore8(wv, off, u32x2{E::pack(R.dva[db][4 * g], R.dva[db][4 * g + 1]),
+                             E::pack(R.dva[db][4 * g + 2], R.dva[db][4 * g + 3])});
+      bstore8(wk, off, u32x2{E::pack(R.dka[db][4 * g] * scale, R.dka[db][4 * g + 1] * scale),
+                             E::pack(R.dka[db][4 * g + 2] * scale, R.dka[db][4 * g + 3] * scale)});
     }
 }
 
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void bf16_dkdv_kernel(
 //   S^T = K Q^T, dP^T = V dO^T      C[key][query]; K, V rows from LDS in
 //                                   perm_row order (8 consecutive keys per
 //                                   lane in registers 8t..8t+7)
-//   dS^T (f32) -> bf16               the B operand of
+//   dS^T (f32) -> 16-bit             the B operand of
 //   dQ^T += K^T dS^T                 C[d][query]; K^T via LDS transpose reads
 template <int HS>
 struct DqCfg {
@@ -330,7 +331,7 @@ struct DqCfg {
 // 16t + e > dn = n - 8h.
 enum DqTile { kFull = 0, kDiagLo = 1, kDiagHi = 2 };
 
-template <int HS, int KIND>
+template <class E, int HS, int KIND>
 __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, int dn, float c,
                                         float lse2, float Dq, const LaneOffsets<HS>& L,
                                         const u32x4 (&qf)[HS / 16], const u32x4 (&gf)[HS / 16],
@@ -344,8 +345,8 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEP; ++ks) {
-      st = mfma32(op_nat<HS>(Kb, L, kb * 32, ks), qf[ks], st);
-      dpt = mfma32(op_nat<HS>(Vb, L, kb * 32, ks), gf[ks], dpt);
+      st = E::mfma(op_nat<HS>(Kb, L, kb * 32, ks), qf[ks], st);
+      dpt = E::mfma(op_nat<HS>(Vb, L, kb * 32, ks), gf[ks], dpt);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -357,7 +358,7 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
         dsv[e] = p * (dpt[8 * t + e] - Dq);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dsp[kb][t][e] = pack_bf16(dsv[2 * e], dsv[2 * e + 1]);
+      for (int e = 0; e < 4; ++e) dsp[kb][t][e] = E::pack(dsv[2 * e], dsv[2 * e + 1]);
     }
   }
 #pragma unroll
@@ -366,7 +367,7 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
-        dqa[db] = mfma32(op_tr<HS>(Kb, L, kb * 32 + 16 * t, db), dsp[kb][t], dqa[db]);
+        dqa[db] = E::mfma(op_tr<HS>(Kb, L, kb * 32 + 16 * t, db), dsp[kb][t], dqa[db]);
   // Scheduling hint: spread the MFMAs over the step, each followed by vector
   // ALU work and LDS reads of other blocks, instead of phase after phase.
 #pragma unroll
@@ -377,8 +378,8 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
   }
 }
 
-template <int HS, bool STRIDED>  // STRIDED as for the dK/dV kernel
-__global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
+template <class E, int HS, bool STRIDED>  // STRIDED as for the dK/dV kernel
+__global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void dq16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, float* __restrict__ Dg,
@@ -430,8 +431,8 @@ __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
     const u32x4 of = bload16(ro, offo);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      dpart = fmaf(bf16lo(of[e]), bf16lo(gf[ks][e]), dpart);
-      dpart = fmaf(bf16hi(of[e]), bf16hi(gf[ks][e]), dpart);
+      dpart = fmaf(E::lo(of[e]), E::lo(gf[ks][e]), dpart);
+      dpart = fmaf(E::hi(of[e]), E::hi(gf[ks][e]), dpart);
     }
   }
   const float Dq = halves_sum(dpart);
@@ -456,11 +457,11 @@ __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
     const int key0 = kt * C::BN;
     if (q0 < T && key0 <= q0) {
       if (key0 == q0)
-        dq_step<HS, kDiagLo>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
+        dq_step<E, HS, kDiagLo>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
       else if (key0 + 32 == q0)
-        dq_step<HS, kDiagHi>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
+        dq_step<E, HS, kDiagHi>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
       else
-        dq_step<HS, kFull>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
+        dq_step<E, HS, kFull>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
     }
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
@@ -476,47 +477,76 @@ __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void bf16_dq_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t off = uint32_t(qrow * rsg + db * 32 + 8 * g + 4 * h) * 2;
-      bstore8(wq, off, u32x2{pack_bf16(dqa[db][4 * g] * scale, dqa[db][4 * g + 1] * scale),
-                             pack_bf16(dqa[db][4 * g + 2] * scale, dqa[db][4 * g + 3] * scale)});
+      bstore8(wq, off, u32x2{E::pack(dqa[db][4 * g] * scale, dqa[db][4 * g + 1] * scale),
+                             E::pack(dqa[db][4 * g + 2] * scale, dqa[db][4 * g + 3] * scale)});
     }
 }
 
 }  // namespace
 
-hipError_t bf16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
+namespace {
+template <class E>
+hipError_t pre16_launch(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
                         float* L2, int BH, int H, int T, int hs, Layout lo, hipStream_t s) {
   const long rows = long(BH) * T;
   const long threads = rows * (hs / 8);
   const dim3 grid(unsigned((threads + kThreads - 1) / kThreads));
-  if (hs == 64)
-    return launch(bf16_pre_kernel<64>, grid, dim3(kThreads), s, o, dO, lse, D, L2, rows, H, T, lo);
-  return launch(bf16_pre_kernel<32>, grid, dim3(kThreads), s, o, dO, lse, D, L2, rows, H, T, lo);
+  auto kern = hs == 64 ? pre16_kernel<E, 64> : pre16_kernel<E, 32>;
+  return launch(kern, grid, dim3(kThreads), s, o, dO, lse, D, L2, rows, H, T, lo);
 }
 
-hipError_t bf16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+template <class E>
+hipError_t dkdv16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
                          uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
                          Layout lo, Layout lg, hipStream_t s) {
   const int bn = DkdvCfg<64>::BN;
   const dim3 grid(unsigned(((T + bn - 1) / bn) * BH));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
-  auto kern = hs == 64 ? (strided ? bf16_dkdv_kernel<64, true> : bf16_dkdv_kernel<64, false>)
-                       : (strided ? bf16_dkdv_kernel<32, true> : bf16_dkdv_kernel<32, false>);
+  auto kern = hs == 64 ? (strided ? dkdv16_kernel<E, 64, true> : dkdv16_kernel<E, 64, false>)
+                       : (strided ? dkdv16_kernel<E, 32, true> : dkdv16_kernel<E, 32, false>);
   return launch(kern, grid, dim3(kThreads), s, q, k, v, dO, D, L2, dk, dv, BH, H, T, scale, li, lo,
                 lg);
 }
 
-hipError_t bf16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+template <class E>
+hipError_t dq16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
                        float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
                        Layout li, Layout lo, Layout lg, hipStream_t s) {
   const int bm = DqCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
-  auto kern = hs == 64 ? (strided ? bf16_dq_kernel<64, true> : bf16_dq_kernel<64, false>)
-                       : (strided ? bf16_dq_kernel<32, true> : bf16_dq_kernel<32, false>);
+  auto kern = hs == 64 ? (strided ? dq16_kernel<E, 64, true> : dq16_kernel<E, 64, false>)
+                       : (strided ? dq16_kernel<E, 32, true> : dq16_kernel<E, 32, false>);
   return launch(kern, grid, dim3(kThreads), s, q, k, v, o, dO, lse, D, L2, dq, BH, H, T, scale, li,
                 lo, lg);
+}
+}  // namespace
+
+hipError_t h16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
+                       float* L2, int BH, int H, int T, int hs, Layout lo, bool f16,
+                       hipStream_t s) {
+  if (f16) return pre16_launch<F16>(o, dO, lse, D, L2, BH, H, T, hs, lo, s);
+  return pre16_launch<Bf16>(o, dO, lse, D, L2, BH, H, T, hs, lo, s);
+}
+
+hipError_t h16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
+                        uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
+                        Layout lo, Layout lg, bool f16, hipStream_t s) {
+  if (f16)
+    return dkdv16_launch<F16>(q, k, v, dO, D, L2, dk, dv, BH, H, T, hs, scale, li, lo, lg, s);
+  return dkdv16_launch<Bf16>(q, k, v, dO, D, L2, dk, dv, BH, H, T, hs, scale, li, lo, lg, s);
+}
+
+hipError_t h16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
+                      float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
+                      Layout li, Layout lo, Layout lg, bool f16, hipStream_t s) {
+  if (f16)
+    return dq16_launch<F16>(q, k, v, o, dO, lse, D, L2, dq, BH, H, T, hs, scale, li, lo, lg, s);
+  return dq16_launch<Bf16>(q, k, v, o, dO, lse, D, L2, dq, BH, H, T, hs, scale, li, lo, lg, s);
 }
 
 }  // namespace gattn

@@ -1,4 +1,5 @@
-// Device helpers for the bf16 kernels: vector types, bf16 <-> f32, MFMA wrappers.
+// Device helpers for the 16-bit (bf16, fp16) MFMA kernels: vector types,
+// element traits (MFMA, pack, unpack), LDS tiles, LDS DMA, rings.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,6 +40,37 @@ __device__ inline f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c)
 // 16*(i/8) + 8*(l/32) + i%8, so each lane's registers 8t..8t+7 cover 8
 // consecutive rows: the k-slot layout of a following MFMA's operand.
 __device__ inline int perm_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Element traits of the 16-bit kernels.  Both types use the same 32x32x16
+// MFMA shape and operand layout (above) and the same LDS tiles; they differ in
+// the MFMA opcode and in the conversions:
+//   mfma(a, b, c) : D += A B with A, B packed 16-bit operands;
+//   pack(x, y)    : two floats -> packed pair (x in the low half), round to
+//                   nearest even (v_cvt_pk_bf16_f32 / v_cvt_pk_f16_f32);
+//   lo(w), hi(w)  : the low / high element of a packed pair as a float.
+struct Bf16 {
+  __device__ static f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return mfma32(a, b, c);
+  }
+  __device__ static uint32_t pack(float x, float y) { return pack_bf16(x, y); }
+  __device__ static float lo(uint32_t w) { return bf16lo(w); }
+  __device__ static float hi(uint32_t w) { return bf16hi(w); }
+};
+struct F16 {
+  __device__ static f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static uint32_t pack(float x, float y) {
+    f16x2 r = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(uint32_t, r);
+  }
+  __device__ static float lo(uint32_t w) { return float(__builtin_bit_cast(f16x2, w)[0]); }
+  __device__ static float hi(uint32_t w) { return float(__builtin_bit_cast(f16x2, w)[1]); }
+};
 
 constexpr float kLog2e = 1.4426950408889634f;
 

@@ -1,4 +1,5 @@
-// bf16 causal attention forward on gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
+// 16-bit (bf16 or fp16) causal attention forward on gfx950 MFMA
+// (v_mfma_f32_32x32x16_bf16 / _f16); E is the element type's traits.
 //
 // Method ("Let's build GPT" summary page): scores are query.key products of
 // earlier tokens (1:06:16) scaled by 1/sqrt(head size) (1:17:18); a
@@ -19,7 +20,7 @@
 //   online softmax in base 2 (running max m and sum l per query = per lane,
 //   so the rescale factor is a per-lane scalar).  A row's reference max m
 //   only moves when the row's maximum exceeds it by more than 2^8 in the
-//   base-2 domain, so the weights stay <= 256 (well inside bf16 and float32 range)
+//   base-2 domain, so the weights stay <= 256 (well inside the 16-bit and float32 ranges)
 //   and the output is rescaled only on those rare tiles;
 //   O^T (hs x queries) += V^T P^T  on MFMA, P^T straight from the S^T
 //                                   accumulators (no LDS round trip), V^T
@@ -33,7 +34,7 @@
 // dropped.
 #include <cmath>
 
-#include "bf16_common.h"
+#include "mfma16_common.h"
 #include "gattn_internal.h"
 
 #ifndef GATTN_FWD_STAGES
@@ -75,7 +76,7 @@ enum TileKind { kFull = 0, kDiagLo = 1, kDiagHi = 2 };
 // One key tile for one wavefront.  `dn` = n - 8h: in the diagonal block,
 // register i of lane (n, h) holds key (q0 + 16*(i/8) + 8h + i%8), which lies
 // above query q0 + n exactly when 16*(i/8) + i%8 > dn.
-template <int HS, int KIND>
+template <class E, int HS, int KIND>
 __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb, int dn, float c,
                                          const LaneOffsets<HS>& L, const u32x4 (&qf)[HS / 16],
                                          FwdState<HS>& st) {
@@ -87,7 +88,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb,
     s[kh] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEP; ++ks)
-      s[kh] = mfma32(op_nat<HS>(Kb, L, kh * 32, ks), qf[ks], s[kh]);
+      s[kh] = E::mfma(op_nat<HS>(Kb, L, kh * 32, ks), qf[ks], s[kh]);
   }
   // Register i of s[kh] is key key0 + kh*32 + 16*(i/8) + 8h + i%8, query q0 + n.
   if (KIND != kFull) {
@@ -127,7 +128,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb,
       for (int e = 0; e < 4; ++e) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e], c, -mc));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e + 1], c, -mc));
-        pf[kh][t][e] = pack_bf16(p0, p1);
+        pf[kh][t][e] = E::pack(p0, p1);
         st.l += p0 + p1;
       }
 #pragma unroll
@@ -136,13 +137,13 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb,
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
-        st.oacc[db] = mfma32(op_tr<HS>(Vb, L, kh * 32 + 16 * t, db), pf[kh][t], st.oacc[db]);
+        st.oacc[db] = E::mfma(op_tr<HS>(Vb, L, kh * 32 + 16 * t, db), pf[kh][t], st.oacc[db]);
 }
 
 // STRIDED = false: q, k, v and o are contiguous (B, H, T, hs) and the row
 // strides are the compile-time HS.
-template <int HS, bool STRIDED>
-__global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __restrict__ q,
+template <class E, int HS, bool STRIDED>
+__global__ __launch_bounds__(kThreads) void fwd16_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
                                                            uint16_t* __restrict__ o,
@@ -203,11 +204,11 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
     const int key0 = kt * C::BN;
     if (q0 < T && key0 <= q0) {  // this wavefront sees some key of the tile
       if (key0 == q0)
-        fwd_tile<HS, kDiagLo>(Ks[buf], Vs[buf], dn, c, L, qf, st);
+        fwd_tile<E, HS, kDiagLo>(Ks[buf], Vs[buf], dn, c, L, qf, st);
       else if (key0 + 32 == q0)
-        fwd_tile<HS, kDiagHi>(Ks[buf], Vs[buf], dn, c, L, qf, st);
+        fwd_tile<E, HS, kDiagHi>(Ks[buf], Vs[buf], dn, c, L, qf, st);
       else
-        fwd_tile<HS, kFull>(Ks[buf], Vs[buf], dn, c, L, qf, st);
+        fwd_tile<E, HS, kFull>(Ks[buf], Vs[buf], dn, c, L, qf, st);
     }
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
@@ -227,8 +228,8 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t off = uint32_t(qrow * rso + db * 32 + 8 * g + 4 * h) * 2;
-      bstore8(wo, off, u32x2{pack_bf16(st.oacc[db][4 * g] * inv, st.oacc[db][4 * g + 1] * inv),
-                             pack_bf16(st.oacc[db][4 * g + 2] * inv, st.oacc[db][4 * g + 3] * inv)});
+      bstore8(wo, off, u32x2{E::pack(st.oacc[db][4 * g] * inv, st.oacc[db][4 * g + 1] * inv),
+                             E::pack(st.oacc[db][4 * g + 2] * inv, st.oacc[db][4 * g + 3] * inv)});
     }
   if (lse != nullptr && h == 0)
     bstoref(make_rsrc(lse + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4,
@@ -237,15 +238,25 @@ __global__ __launch_bounds__(kThreads) void bf16_fwd_kernel(const uint16_t* __re
 
 }  // namespace
 
-hipError_t bf16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                    float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
-                    hipStream_t s) {
+namespace {
+template <class E>
+hipError_t fwd16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                        float* lse, int BH, int H, int T, int hs, float scale, Layout li,
+                        Layout lo, hipStream_t s) {
   const int bm = FwdCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lo);
-  auto kern = hs == 64 ? (strided ? bf16_fwd_kernel<64, true> : bf16_fwd_kernel<64, false>)
-                       : (strided ? bf16_fwd_kernel<32, true> : bf16_fwd_kernel<32, false>);
+  auto kern = hs == 64 ? (strided ? fwd16_kernel<E, 64, true> : fwd16_kernel<E, 64, false>)
+                       : (strided ? fwd16_kernel<E, 32, true> : fwd16_kernel<E, 32, false>);
   return launch(kern, grid, dim3(kThreads), s, q, k, v, o, lse, BH, H, T, scale, li, lo);
+}
+}  // namespace
+
+hipError_t h16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                   float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
+                   bool f16, hipStream_t s) {
+  if (f16) return fwd16_launch<F16>(q, k, v, o, lse, BH, H, T, hs, scale, li, lo, s);
+  return fwd16_launch<Bf16>(q, k, v, o, lse, BH, H, T, hs, scale, li, lo, s);
 }
 
 }  // namespace gattn

@@ -31,6 +31,11 @@
  *   GATTN_BF16: hs in {32, 64}; MFMA kernels, bf16 inputs/outputs, float32
  *               accumulation, every float32 -> bf16 conversion rounds to
  *               nearest even.
+ *   GATTN_F16 : IEEE binary16 (the pages' other half-precision option), same
+ *               kernels and rules as GATTN_BF16 with the fp16 MFMA; the
+ *               softmax weights stay <= 256 and are stored to fp16 only as
+ *               MFMA operands, so no intermediate overflows; outputs whose
+ *               magnitude exceeds 65504 become inf, as any fp16 store does.
  *   GATTN_F32 : any hs in [1, 128]; float32 throughout (deterministic).
  *
  * Ownership: every pointer is a device pointer owned by the caller.  The
@@ -44,7 +49,7 @@
  * before any HIP call, so an invalid call enqueues nothing.  INVALID_ARG: a
  * required pointer is NULL or not 16-byte aligned, B, H or T < 1, hs < 1,
  * scale not finite or <= 0, B*H*T*hs >= 2^31, or dtype unknown.
- * UNSUPPORTED: bf16 with hs not in {32, 64}, or f32 with hs > 128.
+ * UNSUPPORTED: bf16 or fp16 with hs not in {32, 64}, or f32 with hs > 128.
  * WORKSPACE: workspace NULL, not 256-byte aligned, or smaller than
  * gattn_bwd_workspace_bytes().
  * HIP: a kernel launch failed (the HIP error is not cleared from the caller's
@@ -61,7 +66,7 @@
 extern "C" {
 #endif
 
-typedef enum { GATTN_F32 = 0, GATTN_BF16 = 1 } gattn_dtype;
+typedef enum { GATTN_F32 = 0, GATTN_BF16 = 1, GATTN_F16 = 2 } gattn_dtype;
 
 typedef enum {
   GATTN_OK = 0,

@@ -100,6 +100,13 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(f32_to_bf16_bits(x))
 
 
+def round_to_f16(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest IEEE binary16 (numpy's conversion:
+    round to nearest even, overflow to inf), returned as float32."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
 TENSORS = ("q", "k", "v", "do")
 
 
@@ -123,6 +130,8 @@ def normal_tensor(seed: int, shape, scale: float = 1.0, dtype: str = "bf16") -> 
     x = normal_f64(seed, n).astype(np.float32) * np.float32(scale)
     if dtype == "bf16":
         x = round_to_bf16(x)
+    elif dtype == "f16":
+        x = round_to_f16(x)
     elif dtype != "f32":
         raise ValueError(dtype)
     return x.reshape(shape)

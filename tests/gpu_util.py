@@ -14,7 +14,7 @@ OUT_NAMES = ("dq", "dk", "dv", "o", "lse")
 
 def torch_dtype(dtype: str):
     import torch
-    return {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
 
 
 def to_dev(a: np.ndarray, dtype: str):
@@ -31,8 +31,9 @@ def gpu_fwd_bwd(x: dict, dtype: str, scale: float, use_stages: bool = False):
     o = torch.empty_like(t["q"])
     lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
     ga.gattn_fwd(t["q"], t["k"], t["v"], o, lse, scale)
-    ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16 if dtype == "bf16" else ga.F32),
-                     dtype=torch.uint8, device="cuda")
+    code = {"bf16": ga.BF16, "f16": ga.F16, "f32": ga.F32}[dtype]
+    ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, code), dtype=torch.uint8,
+                     device="cuda")
     dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
     if use_stages:
         # row terms from the preprocess stage, dk/dv first, then dq (which
@@ -80,10 +81,11 @@ def pick(got, slices):
 
 
 U_BF16 = 2.0 ** -8  # unit roundoff of bfloat16 (8 significant bits)
+U_F16 = 2.0 ** -11  # unit roundoff of IEEE binary16 (11 significant bits)
 
 
-def rounding_bound(x: dict, scale: float, slices, ref):
-    """First-order bound on the error of the bf16 path, per element, for the
+def rounding_bound(x: dict, scale: float, slices, ref, u: float = U_BF16, slack: float = 1e-3):
+    """First-order bound on the error of a 16-bit path, per element, for the
     selected (b, h) slices, derived from where that path rounds:
       o  = P V           P rounded to bf16 before the MFMA
       dv = P^T dO        P rounded
@@ -91,8 +93,10 @@ def rounding_bound(x: dict, scale: float, slices, ref):
       dq = s dS K        same
     plus the rounding of the stored bf16 output itself (u |ref|).  Terms are
     float64 magnitudes built from the inputs and the oracle's lse:
-    |err| <= u (|ref| + Mag) with Mag = sum of |operand products|."""
-    u = U_BF16
+    |err| <= u (|ref| + Mag) + slack with Mag = sum of |operand products|; u
+    is the unit roundoff of the 16-bit type (bf16 2^-8, fp16 2^-11), `slack`
+    covers the float32 arithmetic (and is the whole bound of lse, which is
+    never rounded to 16 bits)."""
     sel = {n: np.stack([a[b, h] for b, h in slices]) for n, a in x.items()}
     dq_r, dk_r, dv_r, o_r, lse_r = (a[:, 0] for a in ref)
     T = sel["q"].shape[1]
@@ -113,9 +117,9 @@ def rounding_bound(x: dict, scale: float, slices, ref):
     out = []
     for n, r in zip(OUT_NAMES, (dq_r, dk_r, dv_r, o_r, lse_r)):
         if n == "lse":
-            out.append(np.full(r.shape, 1e-3)[:, None])
+            out.append(np.full(r.shape, slack)[:, None])
         else:
-            out.append((u * (np.abs(r) + mag[n]) + 1e-3)[:, None])
+            out.append((u * (np.abs(r) + mag[n]) + slack)[:, None])
     return tuple(out)
 
 

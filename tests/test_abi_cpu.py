@@ -178,3 +178,14 @@ def test_bwd_strided_validation(lib):
     assert f(s_o=_st(T * H * hs, hs, hs - 1)) == INVALID
     assert f(s_g=_st(T * H * hs, hs + 1, H * hs)) == INVALID
     assert f(s_qkv=_st(-1, hs, 3 * H * hs)) == INVALID
+
+
+def test_f16_dtype_code(lib):
+    assert ga.F16 == 2
+    assert ga.gattn_bwd_workspace_bytes(2, 3, 100, 64, ga.F16) == \
+        ga.gattn_bwd_workspace_bytes(2, 3, 100, 64, ga.BF16)
+    assert _fwd(lib, dtype=2, hs=48) == UNSUPPORTED
+    assert _fwd(lib, dtype=2, hs=128) == UNSUPPORTED
+    assert _fwd(lib, dtype=3) == INVALID
+    assert _bwd(lib, dtype=2, hs=16) == UNSUPPORTED
+    assert _bwd(lib, dtype=2, ws=None) == WORKSPACE

@@ -54,3 +54,25 @@ def test_attention_inputs_distinct_tensors():
     assert not np.array_equal(d["q"], d["k"])
     e = si.attention_inputs(1, 2, 8, 4, "f32", seed=1, workload="w", layer=1)
     assert not np.array_equal(d["q"], e["q"])
+
+
+def test_f16_rounding_is_ieee_nearest_even():
+    """The fp16 inputs are IEEE binary16 round-to-nearest-even: ties go to the
+    even mantissa, the largest finite value is 65504, and values from 65520 on
+    round to inf."""
+    u = 2.0 ** -10  # spacing of binary16 in [1, 2)
+    x = np.array([1 + u / 2, 1 + 3 * u / 2, 1 + u / 2 + 2.0 ** -20, -(1 + u / 2), 65504.0,
+                  65519.0, 65520.0, 2.0 ** -24, 2.0 ** -26], dtype=np.float32)
+    want = np.array([1.0, 1 + 2 * u, 1 + u, -1.0, 65504.0, 65504.0, np.inf, 2.0 ** -24, 0.0],
+                    dtype=np.float32)
+    got = si.round_to_f16(x)
+    assert np.array_equal(got, want), (got, want)
+
+
+def test_f16_inputs_are_representable_and_scaled():
+    a = si.attention_inputs(1, 2, 33, 16, "f16", seed=9, workload="pin")
+    b = si.attention_inputs(1, 2, 33, 16, "f32", seed=9, workload="pin")
+    for n in a:
+        assert np.array_equal(a[n], a[n].astype(np.float16).astype(np.float32))
+        # the same draw, rounded: within half an fp16 ulp of the float32 value
+        assert np.all(np.abs(a[n] - b[n]) <= np.abs(b[n]) * 2.0 ** -11 + 2.0 ** -25)
