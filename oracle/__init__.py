@@ -39,6 +39,8 @@ def _load():
     lib.gattn_ref_fwd.restype = None
     lib.gattn_ref_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, ctypes.c_double, i]
     lib.gattn_ref_bwd.restype = None
+    lib.gattn_ref_fwd_kv.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, ctypes.c_double, i]
+    lib.gattn_ref_fwd_kv.restype = None
     lib.gattn_ref_hardware_threads.argtypes = []
     lib.gattn_ref_hardware_threads.restype = i
     _lib = lib
@@ -67,6 +69,22 @@ def attention_forward(q, k, v, scale: float, nthreads: int = 0):
     lse = np.empty((B, H, T), dtype=np.float64)
     lib.gattn_ref_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, T, hs, float(scale),
                       int(nthreads))
+    return o, lse
+
+
+def attention_forward_kv(q, k, v, scale: float, nthreads: int = 0):
+    """Forward of the newest Tq tokens: q (B, H, Tq, hs) against k, v
+    (B, H, Tk, hs), Tk >= Tq; query i sees keys j <= Tk - Tq + i.  Returns
+    (o, lse) in float64."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Tq, hs = q.shape
+    Tk = k.shape[2]
+    assert k.shape == (B, H, Tk, hs) and v.shape == k.shape and Tk >= Tq
+    o = np.empty_like(q)
+    lse = np.empty((B, H, Tq), dtype=np.float64)
+    lib.gattn_ref_fwd_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Tq, Tk, hs,
+                         float(scale), int(nthreads))
     return o, lse
 
 

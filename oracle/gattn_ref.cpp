@@ -24,6 +24,10 @@
 //   dQ_i  = scale * sum_{j<=i} dS_ij k_j
 //   dK_j  = scale * sum_{i>=j} dS_ij q_i
 // Layout: contiguous (B, H, T, hs), hs innermost; lse (B, H, T).
+// gattn_ref_fwd_kv: the forward of the newest Tq tokens of a Tk-token
+// sequence (q for those tokens, k and v for all of them); the pages' generate
+// recomputes the whole forward per token instead (no key/value cache,
+// "nanoGPT" notes section 5), whose last rows this equals.
 // The full probability matrix is kept per slice: no recompute, no blocking.
 
 #include <algorithm>
@@ -103,6 +107,35 @@ void backward_slice(const Slice& x, int T, int hs, double scale, const std::vect
     }
 }
 
+// Forward of Tq queries against Tk >= Tq keys for one slice: query i is the
+// token at position Tk - Tq + i of the key sequence (the newest Tq tokens)
+// and sees keys j <= Tk - Tq + i.  Same arithmetic, in the same order, as
+// forward_slice for each row.
+void forward_slice_kv(const double* q, const double* k, const double* v, double* o, double* lse,
+                      int Tq, int Tk, int hs, double scale) {
+  const double neg_inf = -std::numeric_limits<double>::infinity();
+  const int off = Tk - Tq;
+  std::vector<double> s(Tk), p(Tk);
+  for (int i = 0; i < Tq; ++i) {
+    const int last = off + i;  // newest visible key
+    double m = neg_inf;
+    for (int j = 0; j < Tk; ++j) {
+      s[j] = (j <= last) ? scale * dot(q + (size_t)i * hs, k + (size_t)j * hs, hs) : neg_inf;
+      m = std::max(m, s[j]);
+    }
+    double z = 0.0;
+    for (int j = 0; j <= last; ++j) z += std::exp(s[j] - m);
+    for (int j = 0; j < Tk; ++j) p[j] = (j <= last) ? std::exp(s[j] - m) / z : 0.0;
+    double* orow = o + (size_t)i * hs;
+    for (int d = 0; d < hs; ++d) {
+      double acc = 0.0;
+      for (int j = 0; j <= last; ++j) acc += p[j] * v[(size_t)j * hs + d];
+      orow[d] = acc;
+    }
+    if (lse) lse[i] = m + std::log(z);
+  }
+}
+
 template <class F>
 void parallel_slices(int nslices, int nthreads, F&& f) {
   if (nthreads <= 0) nthreads = (int)std::max(1u, std::thread::hardware_concurrency());
@@ -132,6 +165,18 @@ void gattn_ref_fwd(const double* q, const double* k, const double* v, double* o,
             lse ? lse + (size_t)s * T : nullptr, nullptr, nullptr, nullptr};
     std::vector<double> p((size_t)T * T);
     forward_slice(x, T, hs, scale, p);
+  });
+}
+
+// Forward of the newest Tq tokens against Tk >= Tq keys (decoding with the
+// keys and values of earlier tokens kept): q, o (B,H,Tq,hs); k, v (B,H,Tk,hs);
+// lse (B,H,Tq), may be null.  Query i sees keys j <= Tk - Tq + i.
+void gattn_ref_fwd_kv(const double* q, const double* k, const double* v, double* o, double* lse,
+                      int B, int H, int Tq, int Tk, int hs, double scale, int nthreads) {
+  const size_t sq = (size_t)Tq * hs, sk = (size_t)Tk * hs;
+  parallel_slices(B * H, nthreads, [&](int s) {
+    forward_slice_kv(q + s * sq, k + s * sk, v + s * sk, o + s * sq,
+                     lse ? lse + (size_t)s * Tq : nullptr, Tq, Tk, hs, scale);
   });
 }
 

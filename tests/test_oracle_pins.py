@@ -242,3 +242,38 @@ def test_threads_do_not_change_results():
     b = oracle.attention_backward(q, k, v, dO, 0.35, nthreads=4)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+# ------------------------------------------------ newest-Tq-tokens forward (decode)
+def test_kv_forward_equal_lengths_is_the_causal_forward():
+    """Tq = Tk: every query sees keys j <= i, the forward itself, bit for bit."""
+    rng = np.random.default_rng(11)
+    q, k, v = (rng.standard_normal((2, 3, 37, 8)) for _ in range(3))
+    o, lse = oracle.attention_forward(q, k, v, 0.4)
+    o2, lse2 = oracle.attention_forward_kv(q, k, v, 0.4)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+@pytest.mark.parametrize("Tq", [1, 2, 7, 30])
+def test_kv_forward_is_the_last_rows_of_the_full_forward(Tq):
+    """The pages' generate recomputes the whole forward and keeps the last
+    positions; the newest-Tq forward must equal those rows exactly."""
+    rng = np.random.default_rng(12 + Tq)
+    Tk = 30
+    q, k, v = (rng.standard_normal((2, 2, Tk, 5)) for _ in range(3))
+    o, lse = oracle.attention_forward(q, k, v, 0.7)
+    o2, lse2 = oracle.attention_forward_kv(q[:, :, Tk - Tq:], k, v, 0.7)
+    assert np.array_equal(o[:, :, Tk - Tq:], o2) and np.array_equal(lse[:, :, Tk - Tq:], lse2)
+
+
+def test_kv_forward_single_query_is_plain_softmax_attention():
+    """Tq = 1: the newest token sees every key, softmax(scale q K^T) V."""
+    rng = np.random.default_rng(13)
+    q = rng.standard_normal((1, 2, 1, 6))
+    k, v = (rng.standard_normal((1, 2, 19, 6)) for _ in range(2))
+    o, lse = oracle.attention_forward_kv(q, k, v, 0.5)
+    s = 0.5 * np.einsum("bhd,bhjd->bhj", q[:, :, 0], k)
+    w = np.exp(s - s.max(-1, keepdims=True))
+    ref = np.einsum("bhj,bhjd->bhd", w / w.sum(-1, keepdims=True), v)
+    assert np.allclose(o[:, :, 0], ref, rtol=1e-13, atol=1e-13)
+    assert np.allclose(lse[:, :, 0], np.log(np.exp(s).sum(-1)), rtol=1e-13, atol=1e-13)
