@@ -192,9 +192,151 @@ class HipTimer:
         return ms.value
 
 
+def decode_main(args) -> int:
+    """--mode decode: one decode step per layer at the GPT-2 shape (B=12, H=12,
+    hs=64, 12 layers): the newest token against Tk = args.kv_len cached keys and
+    values (gattn_fwd_decode), HBM-bound; value = bytes of q, k, v read and o
+    written per second.  --mode generate: the pages' generate at the character-
+    level shape (B=1, 6 heads, hs 64, 6 layers, block size 256): the whole
+    forward recomputed at every prefix length T = 1..256 (gattn_fwd, no lse),
+    against decoding the newest token with the earlier keys and values kept."""
+    import numpy as np
+    import torch
+
+    import causal_self_attention_sdpa_amd as ga
+    import synth_inputs as si
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
+    dcode = ga.BF16 if args.dtype == "bf16" else ga.F16
+    lib = ga.load_library()
+    sp = torch.cuda.current_stream().cuda_stream
+    p = lambda x: x.data_ptr()
+    timer = HipTimer()
+
+    def inputs(B, H, T, hs, l, tag):
+        x = si.attention_inputs(B, H, T, hs, args.dtype, seed=2024, workload=tag, layer=l)
+        return {n: torch.from_numpy(a).to(dev).to(tdt) for n, a in x.items()}
+
+    if args.mode == "decode":
+        B, H, hs, L, Tk = 12, 12, 64, 12, args.kv_len
+        scale = 1.0 / math.sqrt(hs)
+        layers = []
+        for l in range(L):
+            t = inputs(B, H, Tk, hs, l, "decode-gpt2")
+            t["q1"] = t["q"][:, :, Tk - 1:].contiguous()
+            t["o"] = torch.empty_like(t["q1"])
+            nb = ga.gattn_fwd_decode_workspace_bytes(B, H, 1, Tk, hs, dcode)
+            t["ws"] = torch.empty(nb, dtype=torch.uint8, device=dev)
+            layers.append(t)
+        calls = [(lib.gattn_fwd_decode, (p(t["q1"]), p(t["k"]), p(t["v"]), p(t["o"]), None, B, H,
+                                         1, Tk, hs, scale, dcode, None, None, None, p(t["ws"]),
+                                         t["ws"].numel(), sp)) for t in layers]
+        ev = [(timer.event(), timer.event()) for _ in range(args.steps)]
+
+        def step(rec):
+            for l, (fn, a) in enumerate(calls):
+                if rec is not None and l == rec % L:
+                    timer.record(ev[rec][0], sp)
+                if fn(*a) != 0:
+                    raise RuntimeError("gattn_fwd_decode failed")
+                if rec is not None and l == rec % L:
+                    timer.record(ev[rec][1], sp)
+
+        for _ in range(args.warmup):
+            step(None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for st in range(args.steps):
+            step(st)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        per_call = float(np.mean([timer.elapsed_ms(a, b) for a, b in ev])) * 1e3
+        alg = (2 * Tk + 2) * B * H * hs * 2  # k, v read; q read, o written
+        out = {"metric": f"decode attention HBM GB/s (one token, {Tk} cached keys) at B{B} H{H} hs{hs}",
+               "value": round(alg * L / dt / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4),
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+               "dtype": args.dtype, "data": "synthetic",
+               "config": {"workload": "GPT-2 124M attention, one decode step per layer",
+                          "B": B, "H": H, "Tq": 1, "Tk": Tk, "hs": hs, "layers": L,
+                          "parallelism": "single GPU"},
+               "us_per_call": round(per_call, 2),
+               "roofline": {"kernel": "dec16_kernel + dec16_combine (one gattn_fwd_decode call)",
+                            "bound": "hbm", "achieved": round(alg / (per_call * 1e-6) / 1e9, 1),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(alg / (per_call * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "traffic": None, "algorithmic_bytes_per_launch": alg}}
+        print(json.dumps(out), flush=True)
+        return 0
+
+    # generate: the pages' recompute-everything loop vs decoding with kept keys/values
+    B, H, hs, L, Tmax = 1, 6, 64, 6, 256
+    scale = 1.0 / math.sqrt(hs)
+    layers = [inputs(B, H, Tmax, hs, l, "generate-char") for l in range(L)]
+    for t in layers:
+        t["o"] = torch.empty_like(t["q"])
+        t["ws"] = torch.empty(max(1, ga.gattn_fwd_decode_workspace_bytes(B, H, 1, Tmax, hs, dcode)),
+                              dtype=torch.uint8, device=dev)
+        t["o1"] = torch.empty((B, H, 1, hs), dtype=tdt, device=dev)
+    # prefix views (contiguous per prefix length T: rows 0..T-1 of each slice)
+    pre = [[{n: t[n][:, :, :T].contiguous() for n in ("q", "k", "v")} for T in range(1, Tmax + 1)]
+           for t in layers]
+    kv_strides = (ctypes.c_int64 * 3)(H * Tmax * hs, Tmax * hs, hs)  # also row T-1 of q
+
+    def recompute():
+        for T in range(1, Tmax + 1):
+            for l in range(L):
+                x = pre[l][T - 1]
+                if lib.gattn_fwd(p(x["q"]), p(x["k"]), p(x["v"]), p(layers[l]["o"]), None, B, H, T,
+                                 hs, scale, dcode, sp) != 0:
+                    raise RuntimeError("gattn_fwd failed")
+
+    def cached():
+        for T in range(1, Tmax + 1):
+            for l in range(L):
+                t = layers[l]
+                q1 = t["q"][:, :, T - 1:T]
+                if lib.gattn_fwd_decode(p(q1), p(t["k"]), p(t["v"]), p(t["o1"]), None, B, H, 1, T,
+                                        hs, scale, dcode, kv_strides, kv_strides, None,
+                                        p(t["ws"]), t["ws"].numel(), sp) != 0:
+                    raise RuntimeError("gattn_fwd_decode failed")
+
+    res = {}
+    for name, fn in (("recompute", recompute), ("cached", cached)):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        reps = max(1, args.steps // 10)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) / reps
+    out = {"metric": "attention time to generate 256 tokens, char-level shape (B1 H6 hs64, 6 layers)",
+           "value": round(res["recompute"] * 1e3, 3), "unit": "ms", "n_gpus": 1,
+           "steps": max(1, args.steps // 10), "warmup": max(1, args.warmup),
+           "ms_per_step": round(res["recompute"] * 1e3, 3), "higher_is_better": False,
+           "scaling": "weak", "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+           "config": {"workload": "the pages' generate: whole forward at every prefix length",
+                      "B": B, "H": H, "hs": hs, "layers": L, "block_size": Tmax,
+                      "parallelism": "single GPU"},
+           "cached_decode_ms": round(res["cached"] * 1e3, 3),
+           "us_per_layer_call": {"recompute": round(res["recompute"] / (Tmax * L) * 1e6, 2),
+                                 "cached": round(res["cached"] / (Tmax * L) * 1e6, 2)},
+           "roofline": None}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--mode", choices=("train", "decode", "generate"), default="train",
+                    help="train: forward + backward (the metric); decode: one new token per "
+                         "layer against --kv-len kept keys; generate: the pages' generate loop")
+    ap.add_argument("--kv-len", type=int, default=1024)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2-124m")
     ap.add_argument("--dtype", choices=("bf16", "f16"), default="bf16",
                     help="16-bit storage type of q, k, v, o and the gradients")
@@ -218,6 +360,9 @@ def main() -> int:
               "(the attention core shards over (b, h) with no exchange; see the design notes).",
               file=sys.stderr)
         return 2
+
+    if args.mode != "train":
+        return decode_main(args)
 
     import numpy as np
     import torch

@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     GattnError,
     attention_backward,
     attention_backward_qkv,
+    attention_decode,
     attention_forward,
     attention_forward_qkv,
     gattn_bwd,
@@ -29,6 +30,8 @@ from ._binding import (  # noqa: F401
     gattn_bwd_strided,
     gattn_bwd_workspace_bytes,
     gattn_fwd,
+    gattn_fwd_decode,
+    gattn_fwd_decode_workspace_bytes,
     gattn_fwd_strided,
     gattn_status_string,
     library_path,

@@ -53,6 +53,10 @@ def load_library():
     lib.gattn_fwd_strided.restype = i
     lib.gattn_bwd_strided.argtypes = [vp] * 9 + [i, i, i, i, f, i, vp, sz, vp, vp, vp, vp]
     lib.gattn_bwd_strided.restype = i
+    lib.gattn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.gattn_fwd_decode_workspace_bytes.restype = sz
+    lib.gattn_fwd_decode.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, vp, vp, vp, vp, sz, vp]
+    lib.gattn_fwd_decode.restype = i
     lib.gattn_status_string.argtypes = [i]
     lib.gattn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -223,6 +227,47 @@ def gattn_bwd_strided(q, k, v, o, dO, lse, dq, dk, dv, scale: float, workspace,
                                  _strides_arg(qkv, "q, k, v"), _strides_arg(od, "o, dO"),
                                  _strides_arg(gr, "dq, dk, dv"), _stream(stream)),
            "gattn_bwd_strided")
+
+
+def gattn_fwd_decode_workspace_bytes(B: int, H: int, Tq: int, Tk: int, hs: int,
+                                     dtype: int) -> int:
+    return int(load_library().gattn_fwd_decode_workspace_bytes(B, H, Tq, Tk, hs, dtype))
+
+
+def gattn_fwd_decode(q, k, v, o, lse, scale: float, workspace=None, stream=None) -> None:
+    """Forward of the newest Tq tokens: q, o (B, H, Tq, hs) and k, v (B, H, Tk,
+    hs) views (hs contiguous; k and v share strides, e.g. the first Tk rows of
+    a key/value cache), Tk >= Tq; query i sees keys j <= Tk - Tq + i.  lse
+    (B, H, Tq) contiguous or None.  The 16-bit path needs a workspace of
+    gattn_fwd_decode_workspace_bytes() bytes (allocated here if None)."""
+    lib = load_library()
+    B, H, Tq, hs = _shape4(q)
+    Tk = int(k.shape[2])
+    dt = _dtype_code(q)
+    qv = _view(q, "q", q.shape, q.dtype)
+    kvv = [_view(x, n, (B, H, Tk, hs), q.dtype) for x, n in ((k, "k"), (v, "v"))]
+    ov = _view(o, "o", q.shape, q.dtype)
+    lp = None if lse is None else _dev(lse, "lse", (B, H, Tq), _torch().float32)
+    need = gattn_fwd_decode_workspace_bytes(B, H, Tq, Tk, hs, dt)
+    if workspace is None and need > 0:
+        workspace = _torch().empty(need, dtype=_torch().uint8, device=q.device)
+    ws = None if workspace is None else _dev(workspace, "workspace")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.gattn_fwd_decode(qv[0], kvv[0][0], kvv[1][0], ov[0], lp, B, H, Tq, Tk, hs,
+                                float(scale), dt, _strides_arg([qv], "q"),
+                                _strides_arg(kvv, "k, v"), _strides_arg([ov], "o"), ws, nbytes,
+                                _stream(stream)), "gattn_fwd_decode")
+
+
+def attention_decode(q, k, v, scale=None, need_lse: bool = False, workspace=None, stream=None):
+    """Returns (o, lse) of the newest Tq tokens q (B, H, Tq, hs) against k, v
+    (B, H, Tk, hs) views; lse is None unless asked for."""
+    torch = _torch()
+    B, H, Tq, hs = _shape4(q)
+    o = torch.empty((B, H, Tq, hs), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device) if need_lse else None
+    gattn_fwd_decode(q, k, v, o, lse, _default_scale(hs, scale), workspace, stream)
+    return o, lse
 
 
 def _qkv_views(qkv, n_head: int):

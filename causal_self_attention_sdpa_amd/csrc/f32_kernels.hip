@@ -60,27 +60,30 @@ __device__ inline float row_dot(const float (&a)[NPL], const float* __restrict__
   return s;
 }
 
-// One wavefront per query row.
+// One wavefront per query row.  Tq queries against Tk >= Tq keys: query i
+// is the token at position Tk - Tq + i and sees keys j <= Tk - Tq + i
+// (Tq = Tk: the causal forward).
 template <int NPL>
 __global__ __launch_bounds__(64 * kWaves) void f32_fwd_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int BH, int H, int T, int hs, float scale,
-    Layout li, Layout lo) {
+    float* __restrict__ o, float* __restrict__ lse, int BH, int H, int Tq, int Tk, int hs,
+    float scale, Layout lq, Layout lk, Layout lo) {
   const int lane = threadIdx.x & 63;
   const long row = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  if (row >= long(BH) * T) return;  // uniform per wavefront
-  const int bh = int(row / T);
-  const int i = int(row - long(bh) * T);
-  const int64_t si = slice_offset(li, bh, H);
-  const float* kb = k + si;
-  const float* vb = v + si;
+  if (row >= long(BH) * Tq) return;  // uniform per wavefront
+  const int bh = int(row / Tq);
+  const int i = int(row - long(bh) * Tq);
+  const int64_t sk = slice_offset(lk, bh, H);
+  const float* kb = k + sk;
+  const float* vb = v + sk;
   float qr[NPL], acc[NPL];
-  load_row<NPL>(q + si + i * li.st, hs, lane, qr);
+  load_row<NPL>(q + slice_offset(lq, bh, H) + i * lq.st, hs, lane, qr);
 #pragma unroll
   for (int e = 0; e < NPL; ++e) acc[e] = 0.f;
   float m = -INFINITY, l = 0.f;
-  for (int j = 0; j <= i; ++j) {
-    const float s = wave_sum(row_dot<NPL>(qr, kb + j * li.st, hs, lane)) * scale;
+  const int last = Tk - Tq + i;
+  for (int j = 0; j <= last; ++j) {
+    const float s = wave_sum(row_dot<NPL>(qr, kb + j * lk.st, hs, lane)) * scale;
     const float mn = fmaxf(m, s);
     const float alpha = expf(m - mn);  // m = -inf on the first key: alpha = 0
     const float p = expf(s - mn);
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(64 * kWaves) void f32_fwd_kernel(
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
       int d = lane + 64 * e;
-      float vv = d < hs ? vb[j * li.st + d] : 0.f;
+      float vv = d < hs ? vb[j * lk.st + d] : 0.f;
       acc[e] = fmaf(p, vv, acc[e] * alpha);
     }
     m = mn;
@@ -222,12 +225,11 @@ dim3 rows_grid(int BH, int T) {
 }  // namespace
 
 hipError_t f32_fwd(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
-                   int H, int T, int hs, float scale, Layout li, Layout lo, hipStream_t s) {
-  if (hs <= 64)
-    return launch(f32_fwd_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, o, lse, BH,
-                  H, T, hs, scale, li, lo);
-  return launch(f32_fwd_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, o, lse, BH, H,
-                T, hs, scale, li, lo);
+                   int H, int Tq, int Tk, int hs, float scale, Layout lq, Layout lk, Layout lo,
+                   hipStream_t s) {
+  auto kern = hs <= 64 ? f32_fwd_kernel<1> : f32_fwd_kernel<2>;
+  return launch(kern, rows_grid(BH, Tq), dim3(64 * kWaves), s, q, k, v, o, lse, BH, H, Tq, Tk, hs,
+                scale, lq, lk, lo);
 }
 
 hipError_t f32_bwd_pre(const float* o, const float* dO, const float* lse, float* D, float* L2,

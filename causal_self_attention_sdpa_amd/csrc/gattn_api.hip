@@ -77,7 +77,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (dtype == GATTN_F32)
     return status_of(gattn::f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
                                     static_cast<const float*>(v), static_cast<float*>(o), lse, BH,
-                                    H, T, hs, scale, li, lo, stream));
+                                    H, T, T, hs, scale, li, li, lo, stream));
   return status_of(gattn::h16_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                   static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
                                   BH, H, T, hs, scale, li, lo, dtype == GATTN_F16, stream));
@@ -186,6 +186,46 @@ int gattn_fwd_strided(const void* q, const void* k, const void* v, void* o, floa
   if (int st = layout_of(qkv_strides, H, T, hs, dtype, li)) return st;
   if (int st = layout_of(o_strides, H, T, hs, dtype, lo)) return st;
   return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, li, lo, stream);
+}
+
+size_t gattn_fwd_decode_workspace_bytes(int B, int H, int Tq, int Tk, int hs, int dtype) {
+  if (Tk < Tq || check_shape(B, H, Tk, hs, dtype) != GATTN_OK) return 0;
+  if (dtype == GATTN_F32) return 0;
+  const gattn::DecodeSplit d = gattn::decode_split(B * H, Tq, Tk);
+  if (d.nsplit == 1) return 0;  // one split: the result is written directly
+  return gattn::decode_opart_bytes(B * H, Tq, hs, d) + gattn::decode_lpart_bytes(B * H, Tq, d);
+}
+
+int gattn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Tq, int Tk, int hs, float scale, int dtype,
+                     const int64_t* q_strides, const int64_t* kv_strides,
+                     const int64_t* o_strides, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o)) return GATTN_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 16)) return GATTN_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return GATTN_ERR_INVALID_ARG;
+  if (Tq < 1 || Tk < Tq) return GATTN_ERR_INVALID_ARG;
+  if (int st = check_shape(B, H, Tk, hs, dtype)) return st;
+  gattn::Layout lq, lk, lo;
+  if (int st = layout_of(q_strides, H, Tq, hs, dtype, lq)) return st;
+  if (int st = layout_of(kv_strides, H, Tk, hs, dtype, lk)) return st;
+  if (int st = layout_of(o_strides, H, Tq, hs, dtype, lo)) return st;
+  const int BH = B * H;
+  if (dtype == GATTN_F32)
+    return status_of(gattn::f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
+                                    static_cast<const float*>(v), static_cast<float*>(o), lse, BH,
+                                    H, Tq, Tk, hs, scale, lq, lk, lo, stream));
+  const size_t need = gattn_fwd_decode_workspace_bytes(B, H, Tq, Tk, hs, dtype);
+  if (need > 0 && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
+    return GATTN_ERR_WORKSPACE;
+  const gattn::DecodeSplit d = gattn::decode_split(BH, Tq, Tk);
+  float* opart = static_cast<float*>(workspace);
+  float* lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          gattn::decode_opart_bytes(BH, Tq, hs, d));
+  return status_of(gattn::h16_fwd_decode(
+      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, BH, H, Tq, Tk, hs, scale,
+      lq, lk, lo, opart, lpart, d, dtype == GATTN_F16, stream));
 }
 
 int gattn_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int T,

@@ -54,6 +54,40 @@ __host__ __device__ inline uint32_t slice_span_bytes(const Layout& l, int T, int
   return uint32_t((int64_t(T - 1) * l.st + hs) * esize);
 }
 
+// Split of the key range for the forward of the newest Tq tokens (decode):
+// nqb 32-query blocks, nsplit key ranges of tps 64-key tiles each, sized so
+// that about 2048 single-wavefront workgroups cover the GPU.  No split (one
+// workgroup per query block writes the result directly, no merge launch)
+// when a block has at most 4 tiles or there are already 1024 blocks.  The
+// workspace size and the launch both derive from this one function.
+struct DecodeSplit {
+  int nqb, nsplit, tps;
+};
+inline DecodeSplit decode_split(int BH, int Tq, int Tk) {
+  DecodeSplit d;
+  d.nqb = (Tq + 31) / 32;
+  const int ntiles = (Tk + 63) / 64;
+  const long blocks = long(BH) * d.nqb;
+  if (ntiles <= 4 || blocks >= 1024) {
+    d.tps = ntiles;
+    d.nsplit = 1;
+    return d;
+  }
+  int want = int((2048 + blocks - 1) / blocks);
+  want = want < 1 ? 1 : (want > ntiles ? ntiles : want);
+  d.tps = (ntiles + want - 1) / want;
+  d.nsplit = (ntiles + d.tps - 1) / d.tps;
+  return d;
+}
+// Decode workspace: [opart BH*nsplit*Tq*hs f32][lpart BH*nsplit*Tq f32], each
+// part on a 256-byte boundary.
+inline size_t decode_opart_bytes(int BH, int Tq, int hs, const DecodeSplit& d) {
+  return (sizeof(float) * size_t(BH) * d.nsplit * Tq * hs + 255) & ~size_t(255);
+}
+inline size_t decode_lpart_bytes(int BH, int Tq, const DecodeSplit& d) {
+  return (sizeof(float) * size_t(BH) * d.nsplit * Tq + 255) & ~size_t(255);
+}
+
 // Backward workspace: [D = rowsum(dO * O)][L2 = lse * log2(e)], each float32
 // (B, H, T) and starting on a 256-byte boundary.
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -64,8 +98,11 @@ inline size_t ws_part_bytes(int B, int H, int T) {
 // ---- float32 path (any hs <= 128, any T; wave per row; deterministic) ----
 // li: layout of q, k, v; lo: of o, dO; lg: of dq, dk, dv.  lse, D and L2 are
 // contiguous (B, H, T).
+// f32_fwd: Tq queries against Tk >= Tq keys, query i seeing keys
+// j <= Tk - Tq + i (Tq = Tk: the causal forward); q in layout lq, k and v in lk.
 hipError_t f32_fwd(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
-                   int H, int T, int hs, float scale, Layout li, Layout lo, hipStream_t s);
+                   int H, int Tq, int Tk, int hs, float scale, Layout lq, Layout lk, Layout lo,
+                   hipStream_t s);
 hipError_t f32_bwd_pre(const float* o, const float* dO, const float* lse, float* D, float* L2,
                        int BH, int H, int T, int hs, Layout lo, hipStream_t s);
 hipError_t f32_bwd_dkdv(const float* q, const float* k, const float* v, const float* dO,
@@ -80,6 +117,12 @@ hipError_t f32_bwd_dq(const float* q, const float* k, const float* v, const floa
 hipError_t h16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                    float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
                    bool f16, hipStream_t s);
+// Forward of the newest Tq tokens against Tk >= Tq keys, split over the key
+// range (partials in opart / lpart, then merged into o and lse).
+hipError_t h16_fwd_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                          float* lse, int BH, int H, int Tq, int Tk, int hs, float scale,
+                          Layout lq, Layout lk, Layout lo, float* opart, float* lpart,
+                          const DecodeSplit& ds, bool f16, hipStream_t s);
 hipError_t h16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
                        float* L2, int BH, int H, int T, int hs, Layout lo, bool f16,
                        hipStream_t s);

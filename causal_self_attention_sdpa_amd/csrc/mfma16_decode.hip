@@ -1,0 +1,288 @@
+// 16-bit (bf16 or fp16) forward of the newest Tq tokens against Tk >= Tq keys
+// on gfx950 MFMA: decoding with the keys and values of earlier tokens kept.
+//
+// Query i is the token at position Tk - Tq + i of the key sequence and sees
+// keys j <= Tk - Tq + i: the causal mask of "Let's build GPT" (tril, 48:54;
+// -inf fill, 55:20) aligned on the newest token.  The pages' generate
+// recomputes the whole forward for every new token (no key/value cache,
+// "nanoGPT" notes section 5); the rows computed here are the last Tq rows of
+// that forward.
+//
+// With few queries the work is reading K and V once (HBM-bound), so the key
+// range is split: workgroup (b, h, 32-query block, split s) is one wavefront
+// that streams key tiles [s*tps, ...) of 64 keys through double-buffered
+// swizzled LDS tiles (LDS DMA), runs the forward's tile step (S^T = K Q^T on
+// MFMA, base-2 online softmax, O^T += V^T P^T) and writes its normalised
+// partial output and log-sum-exp in float32.  dec16_combine merges the
+// splits: lse = log sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s, rounded
+// once to the 16-bit type.  Rows (or whole splits) that see no key keep
+// m = -inf and l = 0 and contribute exp(-inf) = 0; every step is written so
+// that no NaN arises from -inf - (-inf).
+#include <cmath>
+
+#include "gattn_internal.h"
+#include "mfma16_common.h"
+
+namespace gattn {
+namespace {
+
+constexpr int kBN = 64;  // keys per tile
+
+template <int HS>
+struct DecState {
+  f32x16 oacc[HS / 32];
+  float m, l;
+};
+
+// One key tile for a 32-query block.  `last` = newest key visible to this
+// lane's query; MASK: some key of the tile may lie past it.
+template <class E, int HS, bool MASK>
+__device__ __forceinline__ void dec_tile(const uint16_t* Kb, const uint16_t* Vb, int key0, int last,
+                                         int h, float c, const LaneOffsets<HS>& L,
+                                         const u32x4 (&qf)[HS / 16], DecState<HS>& st) {
+  constexpr int KSTEP = HS / 16, DB = HS / 32;
+  f32x16 s[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    s[kh] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks) s[kh] = E::mfma(op_nat<HS>(Kb, L, kh * 32, ks), qf[ks], s[kh]);
+  }
+  // Register i of s[kh] is key key0 + kh*32 + 16*(i/8) + 8h + i%8.
+  if (MASK) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (key0 + kh * 32 + 16 * (i >> 3) + 8 * h + (i & 7) > last) s[kh][i] = -INFINITY;
+  }
+  float mh[2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    mh[kh] = fmaxf(s[kh][0], s[kh][1]);
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) mh[kh] = fmaxf(fmaxf(mh[kh], s[kh][i]), s[kh][i + 1]);
+  }
+  const float mt = halves_max(fmaxf(mh[0], mh[1]));
+  // Lazy rescale as in the forward (the reference max moves only when the
+  // weights would exceed 2^8); a row still at m = -inf takes any finite max.
+  const bool grow = mt > st.m && (st.m == -INFINITY || (mt - st.m) * c > 8.f);
+  if (__builtin_amdgcn_ballot_w64(grow)) {
+    const float alpha = grow ? __builtin_amdgcn_exp2f((st.m - mt) * c) : 1.f;  // -inf -> 0
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) st.oacc[db] *= alpha;
+    st.m = grow ? mt : st.m;
+  }
+  // A row with no visible key so far has every score at -inf: weights 0.
+  const float mc = st.m == -INFINITY ? 0.f : st.m * c;
+  u32x4 pf[2][2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e], c, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e + 1], c, -mc));
+        pf[kh][t][e] = E::pack(p0, p1);
+        st.l += p0 + p1;
+      }
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        st.oacc[db] = E::mfma(op_tr<HS>(Vb, L, kh * 32 + 16 * t, db), pf[kh][t], st.oacc[db]);
+}
+
+// Partials: opart [BH][nsplit][Tq][HS] float32 (normalised output of the
+// split), lpart [BH][nsplit][Tq] float32 (natural log-sum-exp of the split's
+// scores, -inf when the row saw none of its keys).
+// DIRECT (one split): the workgroup's result is the final one; it writes o
+// (16-bit, layout lo) and lse instead of partials.
+template <class E, int HS, bool STRIDED, bool DIRECT>
+__global__ __launch_bounds__(64) void dec16_kernel(const uint16_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ v,
+                                                   float* __restrict__ opart,
+                                                   float* __restrict__ lpart,
+                                                   uint16_t* __restrict__ o,
+                                                   float* __restrict__ lse, int H, int Tq,
+                                                   int Tk, int nqb, int nsplit, int tps,
+                                                   float scale, Layout lq, Layout lk, Layout lo) {
+  constexpr int KSTEP = HS / 16, DB = HS / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * HS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * HS];
+
+  const int lane = threadIdx.x;
+  const int n = lane & 31, h = lane >> 5;
+  const int sp = int(blockIdx.x) % nsplit;
+  const int qb = (int(blockIdx.x) / nsplit) % nqb;
+  const int bh = int(blockIdx.x) / (nsplit * nqb);
+  const int off = Tk - Tq;
+  const int row = qb * 32 + n;
+  const int last = off + row;  // newest key this lane's query sees
+  // Key tiles any query of the block sees, and this split's share of them.
+  const int kmax = off + min(qb * 32 + 31, Tq - 1);
+  const int t0 = sp * tps, t1 = min(kmax / kBN + 1, t0 + tps);
+
+  const int rq = STRIDED ? int(lq.st) : HS, rk = STRIDED ? int(lk.st) : HS;
+  const rsrc_t wq = make_rsrc(q + slice_offset(lq, bh, H), slice_span_bytes(lq, Tq, HS, 2));
+  const int64_t kbase = slice_offset(lk, bh, H);
+  const uint32_t kbytes = slice_span_bytes(lk, Tk, HS, 2);
+  const rsrc_t wk = make_rsrc(k + kbase, kbytes), wv = make_rsrc(v + kbase, kbytes);
+
+  DecState<HS> st;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) st.oacc[db] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  if (t0 < t1) {
+    const float c = scale * kLog2e;
+    const LaneOffsets<HS> L(lane);
+    dma_tile<HS, kBN, 1>(wk, t0 * kBN, rk, Ks[0], 0, lane);
+    dma_tile<HS, kBN, 1>(wv, t0 * kBN, rk, Vs[0], 0, lane);
+    // Q^T as the MFMA B operand (rows past Tq read as zero).
+    u32x4 qf[KSTEP];
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks)
+      qf[ks] = bload16(wq, uint32_t(row * rq + 16 * ks + 8 * h) * 2);
+    wait_vmem();
+    __syncthreads();
+    auto step = [&](int i, auto bufc) {
+      constexpr int buf = decltype(bufc)::value;
+      const int t = t0 + i;
+      if (t + 1 < t1) {
+        dma_tile<HS, kBN, 1>(wk, (t + 1) * kBN, rk, Ks[buf ^ 1], 0, lane);
+        dma_tile<HS, kBN, 1>(wv, (t + 1) * kBN, rk, Vs[buf ^ 1], 0, lane);
+      }
+      const int key0 = t * kBN;
+      if (key0 + kBN - 1 > off + qb * 32)  // some key may lie past some query
+        dec_tile<E, HS, true>(Ks[buf], Vs[buf], key0, last, h, c, L, qf, st);
+      else
+        dec_tile<E, HS, false>(Ks[buf], Vs[buf], key0, last, h, c, L, qf, st);
+      wait_vmem();
+      __syncthreads();
+    };
+    ring_loop<2>(t1 - t0, step);
+  }
+
+  // O^T register i of lane (n, h): column d = db*32 + 8*(i/4) + 4h + i%4 of
+  // this lane's query.  Rows past Tq are dropped by the buffer bounds.
+  const float lt = halves_sum(st.l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if constexpr (DIRECT) {  // split 0 holds key 0, seen by every query: lt > 0
+    const rsrc_t wo = make_rsrc(o + slice_offset(lo, bh, H), slice_span_bytes(lo, Tq, HS, 2));
+    const int ro = STRIDED ? int(lo.st) : HS;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t off = uint32_t(row * ro + db * 32 + 8 * g + 4 * h) * 2;
+        bstore8(wo, off, u32x2{E::pack(st.oacc[db][4 * g] * inv, st.oacc[db][4 * g + 1] * inv),
+                               E::pack(st.oacc[db][4 * g + 2] * inv,
+                                       st.oacc[db][4 * g + 3] * inv)});
+      }
+    if (lse != nullptr && h == 0)
+      bstoref(make_rsrc(lse + long(bh) * Tq, uint32_t(Tq) * 4), uint32_t(row) * 4,
+              st.m * scale + logf(lt));
+    return;
+  }
+  // Normalised partial output and log-sum-exp of the split.
+  const long pbase = (long(bh) * nsplit + sp) * Tq;
+  const rsrc_t wo = make_rsrc(opart + pbase * HS, uint32_t(Tq) * HS * 4);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t o4 = uint32_t(row * HS + db * 32 + 8 * g + 4 * h) * 4;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, f32x4{st.oacc[db][4 * g] * inv, st.oacc[db][4 * g + 1] * inv,
+                                          st.oacc[db][4 * g + 2] * inv,
+                                          st.oacc[db][4 * g + 3] * inv}),
+          wo, o4, 0, 0);
+    }
+  if (h == 0)
+    bstoref(make_rsrc(lpart + pbase, uint32_t(Tq) * 4), uint32_t(row) * 4,
+            lt > 0.f ? st.m * scale + logf(lt) : -INFINITY);
+}
+
+// One wavefront per (b, h, query): merge the splits, store o (16-bit, round
+// to nearest even) and lse.  Lane j holds elements 2j, 2j+1 of the row.
+template <class E, int HS>
+__global__ __launch_bounds__(256) void dec16_combine(const float* __restrict__ opart,
+                                                     const float* __restrict__ lpart,
+                                                     uint16_t* __restrict__ o,
+                                                     float* __restrict__ lse, int BH, int H,
+                                                     int Tq, int nsplit, Layout lo) {
+  const int lane = threadIdx.x & 63;
+  const long gid = long(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (gid >= long(BH) * Tq) return;  // uniform per wavefront
+  const int bh = int(gid / Tq), row = int(gid % Tq);
+  const float* lp = lpart + long(bh) * nsplit * Tq + row;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lp[long(s) * Tq]);
+  // Split 0 holds key 0, which every query sees: M is finite.
+  float Lsum = 0.f, a0 = 0.f, a1 = 0.f;
+  const float* op = opart + (long(bh) * nsplit * Tq + row) * HS + 2 * lane;
+  for (int s = 0; s < nsplit; ++s) {
+    const float w = expf(lp[long(s) * Tq] - M);  // exp(-inf) = 0 for an empty split
+    Lsum += w;
+    if (2 * lane < HS) {
+      const float* x = op + long(s) * Tq * HS;
+      a0 = fmaf(w, x[0], a0);
+      a1 = fmaf(w, x[1], a1);
+    }
+  }
+  const float inv = 1.f / Lsum;
+  if (2 * lane < HS) {
+    uint16_t* orow = o + slice_offset(lo, bh, H) + int64_t(row) * lo.st;
+    *reinterpret_cast<uint32_t*>(orow + 2 * lane) = E::pack(a0 * inv, a1 * inv);
+  }
+  if (lse != nullptr && lane == 0) lse[long(bh) * Tq + row] = M + logf(Lsum);
+}
+
+template <class E, int HS>
+hipError_t dec16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                        float* lse, int BH, int H, int Tq, int Tk, float scale, Layout lq,
+                        Layout lk, Layout lo, float* opart, float* lpart, const DecodeSplit& ds,
+                        hipStream_t s) {
+  const bool strided = !(is_contiguous(lq, H, Tq, HS) && is_contiguous(lk, H, Tk, HS) &&
+                         is_contiguous(lo, H, Tq, HS));
+  const dim3 grid(unsigned(BH * ds.nqb * ds.nsplit));
+  const bool direct = ds.nsplit == 1;
+  auto kern = strided ? (direct ? dec16_kernel<E, HS, true, true> : dec16_kernel<E, HS, true, false>)
+                      : (direct ? dec16_kernel<E, HS, false, true>
+                                : dec16_kernel<E, HS, false, false>);
+  hipError_t e = launch(kern, grid, dim3(64), s, q, k, v, opart, lpart, o, lse, H, Tq, Tk, ds.nqb,
+                        ds.nsplit, ds.tps, scale, lq, lk, lo);
+  if (e != hipSuccess || direct) return e;
+  const long rows = long(BH) * Tq;
+  return launch(dec16_combine<E, HS>, dim3(unsigned((rows + 3) / 4)), dim3(256), s, opart, lpart,
+                o, lse, BH, H, Tq, ds.nsplit, lo);
+}
+
+}  // namespace
+
+hipError_t h16_fwd_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                          float* lse, int BH, int H, int Tq, int Tk, int hs, float scale,
+                          Layout lq, Layout lk, Layout lo, float* opart, float* lpart,
+                          const DecodeSplit& ds, bool f16, hipStream_t s) {
+  if (f16) {
+    if (hs == 64)
+      return dec16_launch<F16, 64>(q, k, v, o, lse, BH, H, Tq, Tk, scale, lq, lk, lo, opart,
+                                   lpart, ds, s);
+    return dec16_launch<F16, 32>(q, k, v, o, lse, BH, H, Tq, Tk, scale, lq, lk, lo, opart, lpart,
+                                 ds, s);
+  }
+  if (hs == 64)
+    return dec16_launch<Bf16, 64>(q, k, v, o, lse, BH, H, Tq, Tk, scale, lq, lk, lo, opart, lpart,
+                                  ds, s);
+  return dec16_launch<Bf16, 32>(q, k, v, o, lse, BH, H, Tq, Tk, scale, lq, lk, lo, opart, lpart,
+                                ds, s);
+}
+
+}  // namespace gattn

@@ -110,6 +110,39 @@ int gattn_fwd_strided(const void* q, const void* k, const void* v, void* o, floa
                       const int64_t* qkv_strides, const int64_t* o_strides, hipStream_t stream);
 
 /*
+ * Forward of the newest Tq tokens against Tk >= Tq keys: decoding with the
+ * keys and values of earlier tokens kept.  Query i is the token at position
+ * Tk - Tq + i of the key sequence and sees keys j <= Tk - Tq + i (the tril
+ * mask, 48:54 / 55:20, aligned on the newest token).  The pages' generate
+ * recomputes the whole forward for every new token instead ("nanoGPT" notes,
+ * section 5: no key/value cache); the rows computed here are the last Tq rows
+ * of that forward.  Tq = Tk is the causal forward.
+ *   q, o    : (B, H, Tq, hs), `dtype`, strides q_strides / o_strides.
+ *   k, v    : (B, H, Tk, hs), `dtype`, one stride set kv_strides: e.g. the
+ *             first Tk rows of a (B, H, Tmax, hs) cache, {H*Tmax*hs, Tmax*hs, hs}.
+ *   lse     : (B, H, Tq) float32, contiguous, may be NULL.
+ *   strides : as in gattn_fwd_strided (NULL = contiguous for that length).
+ *   workspace: at least gattn_fwd_decode_workspace_bytes() bytes, 256-byte
+ *             aligned, overwritten (partial results of the key splits); may be
+ *             NULL when that size is 0 (float32, or a single split).
+ * The 16-bit path splits the key range over workgroups (each streams its keys
+ * from HBM once) and merges the partial results in a second kernel, unless
+ * one split per 32-query block suffices (at most 4 key tiles of 64, or 1024
+ * blocks already); float32 runs one wavefront per query.  INVALID_ARG also
+ * for Tq < 1 or Tk < Tq; WORKSPACE for a missing, misaligned or short
+ * workspace when one is needed.
+ */
+int gattn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Tq, int Tk, int hs, float scale, int dtype,
+                     const int64_t* q_strides, const int64_t* kv_strides,
+                     const int64_t* o_strides, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Workspace bytes gattn_fwd_decode needs (0 for float32 and for arguments it
+ * would reject). */
+size_t gattn_fwd_decode_workspace_bytes(int B, int H, int Tq, int Tk, int hs, int dtype);
+
+/*
  * Bytes of device workspace the backward needs: D = rowsum(dO * o) and
  * lse * log2(e), each float32 (B, H, T) starting on a 256-byte boundary.
  * Returns 0 for arguments gattn_bwd would reject.

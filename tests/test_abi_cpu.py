@@ -189,3 +189,28 @@ def test_f16_dtype_code(lib):
     assert _fwd(lib, dtype=3) == INVALID
     assert _bwd(lib, dtype=2, hs=16) == UNSUPPORTED
     assert _bwd(lib, dtype=2, ws=None) == WORKSPACE
+
+
+def test_decode_validation(lib):
+    def f(q=P, k=P, v=P, o=P, lse=P, B=2, H=3, Tq=1, Tk=1000, hs=64, scale=0.125, dtype=1,
+          sq=None, skv=None, so=None, ws=P, wsb=1 << 24):
+        return lib.gattn_fwd_decode(q, k, v, o, lse, B, H, Tq, Tk, hs, scale, dtype, sq, skv, so,
+                                    ws, wsb, None)
+    assert f(q=None) == INVALID
+    assert f(o=P + 2) == INVALID
+    assert f(lse=P + 4) == INVALID
+    assert f(Tq=0) == INVALID
+    assert f(Tq=1001) == INVALID             # more queries than keys
+    assert f(scale=float("nan")) == INVALID
+    assert f(hs=48) == UNSUPPORTED
+    assert f(dtype=2, hs=16) == UNSUPPORTED
+    assert f(skv=_st(3 * 1000 * 64, 1000 * 64, 32)) == INVALID  # row stride < hs
+    assert f(ws=None) == WORKSPACE            # 1000 keys: split, partials need a workspace
+    assert f(ws=P + 128) == WORKSPACE         # not 256-aligned
+    need = ga.gattn_fwd_decode_workspace_bytes(2, 3, 1, 1000, 64, 1)
+    assert need > 0
+    assert f(wsb=need - 4) == WORKSPACE
+    assert ga.gattn_fwd_decode_workspace_bytes(2, 3, 1, 1000, 64, 0) == 0  # float32: none
+    assert ga.gattn_fwd_decode_workspace_bytes(2, 3, 1, 256, 64, 1) == 0   # 4 tiles: no split
+    assert ga.gattn_fwd_decode_workspace_bytes(2, 3, 5, 4, 64, 1) == 0     # Tq > Tk rejected
+    assert ga.gattn_fwd_decode_workspace_bytes(2, 3, 1, 100, 48, 1) == 0   # unsupported hs
