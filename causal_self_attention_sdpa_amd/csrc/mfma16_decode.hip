@@ -223,18 +223,29 @@ __global__ __launch_bounds__(256) void dec16_combine(const float* __restrict__ o
   if (gid >= long(BH) * Tq) return;  // uniform per wavefront
   const int bh = int(gid / Tq), row = int(gid % Tq);
   const float* lp = lpart + long(bh) * nsplit * Tq + row;
+  // The splits' lse values are read across lanes (one load per lane, not one
+  // dependent load per split), then reduced over the wavefront.
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lp[long(s) * Tq]);
+  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, lp[long(s) * Tq]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   // Split 0 holds key 0, which every query sees: M is finite.
-  float Lsum = 0.f, a0 = 0.f, a1 = 0.f;
+  float Lsum = 0.f;
+  for (int s = lane; s < nsplit; s += 64) Lsum += expf(lp[long(s) * Tq] - M);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) Lsum += __shfl_xor(Lsum, off, 64);
+  // Weighted sum of the partial rows; the loop is unrolled so the loads of
+  // several splits are in flight together.
+  float a0 = 0.f, a1 = 0.f;
   const float* op = opart + (long(bh) * nsplit * Tq + row) * HS + 2 * lane;
+  const bool act = 2 * lane < HS;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) {
     const float w = expf(lp[long(s) * Tq] - M);  // exp(-inf) = 0 for an empty split
-    Lsum += w;
-    if (2 * lane < HS) {
-      const float* x = op + long(s) * Tq * HS;
-      a0 = fmaf(w, x[0], a0);
-      a1 = fmaf(w, x[1], a1);
+    if (act) {
+      const float2 x = *reinterpret_cast<const float2*>(op + long(s) * Tq * HS);
+      a0 = fmaf(w, x.x, a0);
+      a1 = fmaf(w, x.y, a1);
     }
   }
   const float inv = 1.f / Lsum;
