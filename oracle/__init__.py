@@ -12,6 +12,9 @@ query.key affinities (1:06:16) divided by sqrt(head size) (1:17:18), weighted
 sum of values (1:10:15), heads independent (1:22:27).  The backward is the
 chain rule of that forward (the pages only say the model is trained with
 backprop); see the header of `gattn_ref.cpp` for the formulas.
+
+`oracle.dropout` adds attention dropout (float64 numpy, the mask drawn with
+the Philox generator of `oracle.philox`).
 """
 from __future__ import annotations
 
