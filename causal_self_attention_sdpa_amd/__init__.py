@@ -12,6 +12,9 @@ allocate the outputs with torch and call those; `attention_forward_qkv` /
 `attention_backward_qkv` do the same for a GPT block's fused (B, T, 3C)
 projection output, reading q, k, v in place and writing y (B, T, C) and the
 gradient dqkv (B, T, 3C) through the strided entry points.
+`attention_forward_dropout` / `attention_backward_dropout` add dropout on the
+attention weights (mask from a seed and an offset, recomputed in the
+backward, never stored).
 """
 from ._binding import (  # noqa: F401
     BF16,
@@ -19,11 +22,14 @@ from ._binding import (  # noqa: F401
     F32,
     GattnError,
     attention_backward,
+    attention_backward_dropout,
     attention_backward_qkv,
     attention_decode,
     attention_forward,
+    attention_forward_dropout,
     attention_forward_qkv,
     gattn_bwd,
+    gattn_bwd_dropout,
     gattn_bwd_dkdv,
     gattn_bwd_dq,
     gattn_bwd_preprocess,
@@ -31,7 +37,9 @@ from ._binding import (  # noqa: F401
     gattn_bwd_workspace_bytes,
     gattn_fwd,
     gattn_fwd_decode,
+    gattn_dropout_mask,
     gattn_fwd_decode_workspace_bytes,
+    gattn_fwd_dropout,
     gattn_fwd_strided,
     gattn_status_string,
     library_path,

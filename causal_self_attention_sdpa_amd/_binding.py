@@ -57,6 +57,14 @@ def load_library():
     lib.gattn_fwd_decode_workspace_bytes.restype = sz
     lib.gattn_fwd_decode.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, vp, vp, vp, vp, sz, vp]
     lib.gattn_fwd_decode.restype = i
+    u64, u32 = ctypes.c_uint64, ctypes.c_uint32
+    lib.gattn_fwd_dropout.argtypes = [vp] * 5 + [i, i, i, i, f, i, f, u64, u32, vp, vp, vp]
+    lib.gattn_fwd_dropout.restype = i
+    lib.gattn_bwd_dropout.argtypes = ([vp] * 9 + [i, i, i, i, f, i, f, u64, u32, vp, sz]
+                                      + [vp, vp, vp, vp])
+    lib.gattn_bwd_dropout.restype = i
+    lib.gattn_dropout_mask.argtypes = [vp, i, i, i, f, u64, u32, vp]
+    lib.gattn_dropout_mask.restype = i
     lib.gattn_status_string.argtypes = [i]
     lib.gattn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -268,6 +276,78 @@ def attention_decode(q, k, v, scale=None, need_lse: bool = False, workspace=None
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device) if need_lse else None
     gattn_fwd_decode(q, k, v, o, lse, _default_scale(hs, scale), workspace, stream)
     return o, lse
+
+
+def gattn_fwd_dropout(q, k, v, o, lse, scale: float, p: float, seed: int, offset: int,
+                      stream=None) -> None:
+    """As gattn_fwd_strided with attention dropout of probability p; the
+    mask is drawn from (seed, offset) as the C header defines."""
+    lib = load_library()
+    B, H, T, hs = _shape4(q)
+    dt = _dtype_code(q)
+    qkv = [_view(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+    ov = _view(o, "o", q.shape, q.dtype)
+    lp = None if lse is None else _dev(lse, "lse", (B, H, T), _torch().float32)
+    _check(lib.gattn_fwd_dropout(*(x for x, _ in qkv), ov[0], lp, B, H, T, hs, float(scale), dt,
+                                 float(p), int(seed), int(offset),
+                                 _strides_arg(qkv, "q, k, v"), _strides_arg([ov], "o"),
+                                 _stream(stream)), "gattn_fwd_dropout")
+
+
+def gattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, scale: float, p: float, seed: int,
+                      offset: int, workspace, stream=None) -> None:
+    """Backward of gattn_fwd_dropout (same p, seed, offset); strided views as
+    gattn_bwd_strided."""
+    lib = load_library()
+    B, H, T, hs = _shape4(q)
+    dt = _dtype_code(q)
+    qkv = [_view(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
+    od = [_view(x, n, q.shape, q.dtype) for x, n in ((o, "o"), (dO, "dO"))]
+    gr = [_view(x, n, q.shape, q.dtype) for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    lp = _dev(lse, "lse", (B, H, T), _torch().float32)
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.gattn_bwd_dropout(*(x for x, _ in qkv), *(x for x, _ in od), lp,
+                                 *(x for x, _ in gr), B, H, T, hs, float(scale), dt, float(p),
+                                 int(seed), int(offset), ws, nbytes,
+                                 _strides_arg(qkv, "q, k, v"), _strides_arg(od, "o, dO"),
+                                 _strides_arg(gr, "dq, dk, dv"), _stream(stream)),
+           "gattn_bwd_dropout")
+
+
+def gattn_dropout_mask(keep, B: int, H: int, T: int, p: float, seed: int, offset: int,
+                       stream=None) -> None:
+    """Writes the keep decisions (uint8, 1 = kept) into keep (B, H, T, T)."""
+    torch = _torch()
+    kp = _dev(keep, "keep", (B, H, T, T), torch.uint8)
+    _check(load_library().gattn_dropout_mask(kp, B, H, T, float(p), int(seed), int(offset),
+                                             _stream(stream)), "gattn_dropout_mask")
+
+
+def attention_forward_dropout(q, k, v, p: float, seed: int, offset: int = 0, scale=None,
+                              need_lse: bool = True, stream=None):
+    """Returns (o, lse) with attention dropout; lse is None if not needed."""
+    torch = _torch()
+    B, H, T, hs = _shape4(q)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if need_lse else None
+    gattn_fwd_dropout(q, k, v, o, lse, _default_scale(hs, scale), p, seed, offset, stream)
+    return o, lse
+
+
+def attention_backward_dropout(q, k, v, o, dO, lse, p: float, seed: int, offset: int = 0,
+                               scale=None, workspace=None, stream=None):
+    """Returns (dq, dk, dv) of attention_forward_dropout with the same p, seed,
+    offset; allocates the workspace unless one is given."""
+    torch = _torch()
+    B, H, T, hs = _shape4(q)
+    if workspace is None:
+        n = gattn_bwd_workspace_bytes(B, H, T, hs, _dtype_code(q))
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    gattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, _default_scale(hs, scale), p, seed,
+                      offset, workspace, stream)
+    return dq, dk, dv
 
 
 def _qkv_views(qkv, n_head: int):

@@ -16,6 +16,9 @@
 //              summary page 48:54 / 55:20; softmax rows 51:04), scores scaled
 //              by `scale` (1:17:18), values summed with the weights (1:10:15).
 //   backward : chain rule; P is recomputed as exp(s - lse).
+// Dropout (dr.thr != 0, philox.h): weight (i, j) is kept by its own
+// generator decision and kept weights are multiplied by dr.zs in the value
+// sum; the backward uses dV = (P*Z)^T dO, dS = P * (Z * dO V^T - D).
 #include "gattn_internal.h"
 
 #include <cmath>
@@ -67,7 +70,7 @@ template <int NPL>
 __global__ __launch_bounds__(64 * kWaves) void f32_fwd_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int BH, int H, int Tq, int Tk, int hs,
-    float scale, Layout lq, Layout lk, Layout lo) {
+    float scale, Layout lq, Layout lk, Layout lo, Dropout dr) {
   const int lane = threadIdx.x & 63;
   const long row = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (row >= long(BH) * Tq) return;  // uniform per wavefront
@@ -88,15 +91,17 @@ __global__ __launch_bounds__(64 * kWaves) void f32_fwd_kernel(
     const float alpha = expf(m - mn);  // m = -inf on the first key: alpha = 0
     const float p = expf(s - mn);
     l = l * alpha + p;
+    const float pk = dr.thr == 0 || keep_one(uint32_t(last), uint32_t(j), uint32_t(bh), dr) ? p
+                                                                                             : 0.f;
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
       int d = lane + 64 * e;
       float vv = d < hs ? vb[j * lk.st + d] : 0.f;
-      acc[e] = fmaf(p, vv, acc[e] * alpha);
+      acc[e] = fmaf(pk, vv, acc[e] * alpha);
     }
     m = mn;
   }
-  const float inv = 1.f / l;
+  const float inv = (dr.thr == 0 ? 1.f : dr.zs) / l;
   float* orow = o + slice_offset(lo, bh, H) + i * lo.st;
 #pragma unroll
   for (int e = 0; e < NPL; ++e) {
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(64 * kWaves) void f32_dkdv_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ dO, const float* __restrict__ D, const float* __restrict__ L2,
     float* __restrict__ dk, float* __restrict__ dv, int BH, int H, int T, int hs, float scale,
-    Layout li, Layout lo, Layout lg) {
+    Layout li, Layout lo, Layout lg, Dropout dr) {
   const float c = scale * 1.4426950408889634f;
   const int lane = threadIdx.x & 63;
   const long row = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
@@ -154,23 +159,26 @@ __global__ __launch_bounds__(64 * kWaves) void f32_dkdv_kernel(
     float dp = row_dot<NPL>(vr, ob + i * lo.st, hs, lane);
     wave_sum2(s, dp);
     const float p = exp2f(fmaf(s, c, -L2[rb + i]));
-    const float ds = p * (dp - D[rb + i]);
+    const bool kept = dr.thr == 0 || keep_one(uint32_t(i), uint32_t(j), uint32_t(bh), dr);
+    const float pk = kept ? p : 0.f;
+    const float ds = p * ((kept ? dp * (dr.thr == 0 ? 1.f : dr.zs) : 0.f) - D[rb + i]);
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
       int d = lane + 64 * e;
       float qq = d < hs ? qb[i * li.st + d] : 0.f;
       float gg = d < hs ? ob[i * lo.st + d] : 0.f;
-      av[e] = fmaf(p, gg, av[e]);
+      av[e] = fmaf(pk, gg, av[e]);
       ak[e] = fmaf(ds, qq, ak[e]);
     }
   }
+  const float zv = dr.thr == 0 ? 1.f : dr.zs;
   const int64_t go = slice_offset(lg, bh, H) + j * lg.st;
 #pragma unroll
   for (int e = 0; e < NPL; ++e) {
     int d = lane + 64 * e;
     if (d < hs) {
       dk[go + d] = ak[e] * scale;
-      dv[go + d] = av[e];
+      dv[go + d] = av[e] * zv;
     }
   }
 }
@@ -181,7 +189,7 @@ __global__ __launch_bounds__(64 * kWaves) void f32_dq_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ D,
     float* __restrict__ dq, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
-    Layout lg) {
+    Layout lg, Dropout dr) {
   const int lane = threadIdx.x & 63;
   const long row = long(blockIdx.x) * kWaves + (threadIdx.x >> 6);
   if (row >= long(BH) * T) return;
@@ -201,7 +209,8 @@ __global__ __launch_bounds__(64 * kWaves) void f32_dq_kernel(
     float dp = row_dot<NPL>(gr, vb + j * li.st, hs, lane);
     wave_sum2(s, dp);
     const float p = expf(s * scale - li_);
-    const float ds = p * (dp - Di);
+    const bool kept = dr.thr == 0 || keep_one(uint32_t(i), uint32_t(j), uint32_t(bh), dr);
+    const float ds = p * ((kept ? dp * (dr.thr == 0 ? 1.f : dr.zs) : 0.f) - Di);
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
       int d = lane + 64 * e;
@@ -226,10 +235,10 @@ dim3 rows_grid(int BH, int T) {
 
 hipError_t f32_fwd(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
                    int H, int Tq, int Tk, int hs, float scale, Layout lq, Layout lk, Layout lo,
-                   hipStream_t s) {
+                   const Dropout& dr, hipStream_t s) {
   auto kern = hs <= 64 ? f32_fwd_kernel<1> : f32_fwd_kernel<2>;
   return launch(kern, rows_grid(BH, Tq), dim3(64 * kWaves), s, q, k, v, o, lse, BH, H, Tq, Tk, hs,
-                scale, lq, lk, lo);
+                scale, lq, lk, lo, dr);
 }
 
 hipError_t f32_bwd_pre(const float* o, const float* dO, const float* lse, float* D, float* L2,
@@ -244,22 +253,23 @@ hipError_t f32_bwd_pre(const float* o, const float* dO, const float* lse, float*
 hipError_t f32_bwd_dkdv(const float* q, const float* k, const float* v, const float* dO,
                         const float* D, const float* L2, float* dk, float* dv, int BH, int H,
                         int T, int hs, float scale, Layout li, Layout lo, Layout lg,
-                        hipStream_t s) {
+                        const Dropout& dr, hipStream_t s) {
   if (hs <= 64)
     return launch(f32_dkdv_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, D, L2,
-                  dk, dv, BH, H, T, hs, scale, li, lo, lg);
+                  dk, dv, BH, H, T, hs, scale, li, lo, lg, dr);
   return launch(f32_dkdv_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, D, L2, dk,
-                dv, BH, H, T, hs, scale, li, lo, lg);
+                dv, BH, H, T, hs, scale, li, lo, lg, dr);
 }
 
 hipError_t f32_bwd_dq(const float* q, const float* k, const float* v, const float* dO,
                       const float* lse, const float* D, float* dq, int BH, int H, int T, int hs,
-                      float scale, Layout li, Layout lo, Layout lg, hipStream_t s) {
+                      float scale, Layout li, Layout lo, Layout lg, const Dropout& dr,
+                      hipStream_t s) {
   if (hs <= 64)
     return launch(f32_dq_kernel<1>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D,
-                  dq, BH, H, T, hs, scale, li, lo, lg);
+                  dq, BH, H, T, hs, scale, li, lo, lg, dr);
   return launch(f32_dq_kernel<2>, rows_grid(BH, T), dim3(64 * kWaves), s, q, k, v, dO, lse, D, dq,
-                BH, H, T, hs, scale, li, lo, lg);
+                BH, H, T, hs, scale, li, lo, lg, dr);
 }
 
 }  // namespace gattn

@@ -63,6 +63,22 @@ int layout_of(const int64_t* strides, int H, int T, int hs, int dtype, gattn::La
   return GATTN_OK;
 }
 
+// Dropout parameters of probability p (finite, 0 <= p, rounding to a 16-bit
+// threshold of at most 65535); thr = 0 (p rounds to 0) means no dropout.
+int dropout_of(float p, uint64_t seed, uint32_t offset, gattn::Dropout& d) {
+  if (!std::isfinite(p) || p < 0.f || p >= 1.f) return GATTN_ERR_INVALID_ARG;
+  const double t = std::floor(double(p) * 65536.0 + 0.5);
+  if (t > 65535.0) return GATTN_ERR_INVALID_ARG;
+  d.thr = uint32_t(t);
+  d.k0 = uint32_t(seed);
+  d.k1 = uint32_t(seed >> 32);
+  d.off = offset;
+  d.zs = float(65536.0 / (65536.0 - t));
+  return GATTN_OK;
+}
+
+const gattn::Dropout kNoDropout{0, 0, 0, 0, 1.f};
+
 // Workspace parts: D, then L2 = lse * log2(e).
 float* ws_D(void* ws) { return static_cast<float*>(ws); }
 float* ws_L2(void* ws, int B, int H, int T) {
@@ -72,15 +88,15 @@ float* ws_L2(void* ws, int B, int H, int T) {
 // Implementations on layouts (arguments already validated).
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int T, int hs, float scale, int dtype, gattn::Layout li, gattn::Layout lo,
-             hipStream_t stream) {
+             const gattn::Dropout& dr, hipStream_t stream) {
   const int BH = B * H;
   if (dtype == GATTN_F32)
     return status_of(gattn::f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
                                     static_cast<const float*>(v), static_cast<float*>(o), lse, BH,
-                                    H, T, T, hs, scale, li, li, lo, stream));
+                                    H, T, T, hs, scale, li, li, lo, dr, stream));
   return status_of(gattn::h16_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                   static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
-                                  BH, H, T, hs, scale, li, lo, dtype == GATTN_F16, stream));
+                                  BH, H, T, hs, scale, li, lo, dr, dtype == GATTN_F16, stream));
 }
 
 int pre_impl(const void* o, const void* dO, const float* lse, int B, int H, int T, int hs,
@@ -98,7 +114,7 @@ int pre_impl(const void* o, const void* dO, const float* lse, int B, int H, int 
 int dq_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
             const float* lse, void* dq, int B, int H, int T, int hs, float scale, int dtype,
             void* workspace, gattn::Layout li, gattn::Layout lo, gattn::Layout lg,
-            hipStream_t stream) {
+            const gattn::Dropout& dr, hipStream_t stream) {
   float* D = ws_D(workspace);
   float* L2 = ws_L2(workspace, B, H, T);
   if (dtype == GATTN_F32) {
@@ -106,30 +122,31 @@ int dq_impl(const void* q, const void* k, const void* v, const void* o, const vo
     return status_of(gattn::f32_bwd_dq(
         static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
         static_cast<const float*>(dO), lse, D, static_cast<float*>(dq), B * H, H, T, hs, scale, li,
-        lo, lg, stream));
+        lo, lg, dr, stream));
   }
   return status_of(gattn::h16_bwd_dq(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
       static_cast<const uint16_t*>(dO), lse, D, L2, static_cast<uint16_t*>(dq), B * H, H, T, hs,
-      scale, li, lo, lg, dtype == GATTN_F16, stream));
+      scale, li, lo, lg, dr, dtype == GATTN_F16, stream));
 }
 
 int dkdv_impl(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
               int B, int H, int T, int hs, float scale, int dtype, void* workspace,
-              gattn::Layout li, gattn::Layout lo, gattn::Layout lg, hipStream_t stream) {
+              gattn::Layout li, gattn::Layout lo, gattn::Layout lg, const gattn::Dropout& dr,
+              hipStream_t stream) {
   const float* D = ws_D(workspace);
   const float* L2 = ws_L2(workspace, B, H, T);
   if (dtype == GATTN_F32)
     return status_of(gattn::f32_bwd_dkdv(
         static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
         static_cast<const float*>(dO), D, L2, static_cast<float*>(dk), static_cast<float*>(dv),
-        B * H, H, T, hs, scale, li, lo, lg, stream));
+        B * H, H, T, hs, scale, li, lo, lg, dr, stream));
   return status_of(gattn::h16_bwd_dkdv(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), D, L2,
       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B * H, H, T, hs, scale, li, lo, lg,
-      dtype == GATTN_F16, stream));
+      dr, dtype == GATTN_F16, stream));
 }
 
 int check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -175,7 +192,7 @@ int gattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, 
               int T, int hs, float scale, int dtype, hipStream_t stream) {
   if (int st = check_fwd(q, k, v, o, lse, B, H, T, hs, scale, dtype)) return st;
   const gattn::Layout c = gattn::contiguous_layout(H, T, hs);
-  return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, c, c, stream);
+  return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, c, c, kNoDropout, stream);
 }
 
 int gattn_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, int B,
@@ -185,7 +202,30 @@ int gattn_fwd_strided(const void* q, const void* k, const void* v, void* o, floa
   gattn::Layout li, lo;
   if (int st = layout_of(qkv_strides, H, T, hs, dtype, li)) return st;
   if (int st = layout_of(o_strides, H, T, hs, dtype, lo)) return st;
-  return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, li, lo, stream);
+  return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, li, lo, kNoDropout, stream);
+}
+
+int gattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                      int H, int T, int hs, float scale, int dtype, float p, uint64_t seed,
+                      uint32_t offset, const int64_t* qkv_strides, const int64_t* o_strides,
+                      hipStream_t stream) {
+  if (int st = check_fwd(q, k, v, o, lse, B, H, T, hs, scale, dtype)) return st;
+  gattn::Dropout dr;
+  if (int st = dropout_of(p, seed, offset, dr)) return st;
+  gattn::Layout li, lo;
+  if (int st = layout_of(qkv_strides, H, T, hs, dtype, li)) return st;
+  if (int st = layout_of(o_strides, H, T, hs, dtype, lo)) return st;
+  return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, li, lo, dr, stream);
+}
+
+int gattn_dropout_mask(uint8_t* keep, int B, int H, int T, float p, uint64_t seed,
+                       uint32_t offset, hipStream_t stream) {
+  if (keep == nullptr || B < 1 || H < 1 || T < 1) return GATTN_ERR_INVALID_ARG;
+  if (int64_t(B) * H * T * T >= (int64_t(1) << 40) || int64_t(B) * H >= (int64_t(1) << 31))
+    return GATTN_ERR_INVALID_ARG;
+  gattn::Dropout dr;
+  if (int st = dropout_of(p, seed, offset, dr)) return st;
+  return status_of(gattn::dropout_mask(keep, B * H, T, dr, stream));
 }
 
 size_t gattn_fwd_decode_workspace_bytes(int B, int H, int Tq, int Tk, int hs, int dtype) {
@@ -214,7 +254,7 @@ int gattn_fwd_decode(const void* q, const void* k, const void* v, void* o, float
   if (dtype == GATTN_F32)
     return status_of(gattn::f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
                                     static_cast<const float*>(v), static_cast<float*>(o), lse, BH,
-                                    H, Tq, Tk, hs, scale, lq, lk, lo, stream));
+                                    H, Tq, Tk, hs, scale, lq, lk, lo, kNoDropout, stream));
   const size_t need = gattn_fwd_decode_workspace_bytes(B, H, Tq, Tk, hs, dtype);
   if (need > 0 && (workspace == nullptr || !aligned(workspace, 256) || workspace_bytes < need))
     return GATTN_ERR_WORKSPACE;
@@ -245,7 +285,8 @@ int gattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, con
   if (int st = check_main(q, k, v, dO, scale, B, H, T, hs, dtype, workspace, workspace_bytes))
     return st;
   const gattn::Layout c = gattn::contiguous_layout(H, T, hs);
-  return dq_impl(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, workspace, c, c, c, stream);
+  return dq_impl(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, workspace, c, c, c,
+                 kNoDropout, stream);
 }
 
 int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk,
@@ -255,7 +296,8 @@ int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, 
   if (int st = check_main(q, k, v, dO, scale, B, H, T, hs, dtype, workspace, workspace_bytes))
     return st;
   const gattn::Layout c = gattn::contiguous_layout(H, T, hs);
-  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, c, c, c, stream);
+  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, c, c, c,
+                   kNoDropout, stream);
 }
 
 int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -268,9 +310,10 @@ int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
     return st;
   const gattn::Layout c = gattn::contiguous_layout(H, T, hs);
   if (int st = dq_impl(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, workspace, c, c, c,
-                       stream))
+                       kNoDropout, stream))
     return st;
-  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, c, c, c, stream);
+  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, c, c, c, kNoDropout,
+                   stream);
 }
 
 int gattn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -286,9 +329,32 @@ int gattn_bwd_strided(const void* q, const void* k, const void* v, const void* o
   if (int st = layout_of(o_strides, H, T, hs, dtype, lo)) return st;
   if (int st = layout_of(grad_strides, H, T, hs, dtype, lg)) return st;
   if (int st = dq_impl(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, workspace, li, lo, lg,
-                       stream))
+                       kNoDropout, stream))
     return st;
-  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, li, lo, lg, stream);
+  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, li, lo, lg,
+                   kNoDropout, stream);
+}
+
+int gattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int T, int hs,
+                      float scale, int dtype, float p, uint64_t seed, uint32_t offset,
+                      void* workspace, size_t workspace_bytes, const int64_t* qkv_strides,
+                      const int64_t* o_strides, const int64_t* grad_strides,
+                      hipStream_t stream) {
+  if (int st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, T, hs, scale, dtype, workspace,
+                         workspace_bytes))
+    return st;
+  gattn::Dropout dr;
+  if (int st = dropout_of(p, seed, offset, dr)) return st;
+  gattn::Layout li, lo, lg;
+  if (int st = layout_of(qkv_strides, H, T, hs, dtype, li)) return st;
+  if (int st = layout_of(o_strides, H, T, hs, dtype, lo)) return st;
+  if (int st = layout_of(grad_strides, H, T, hs, dtype, lg)) return st;
+  if (int st = dq_impl(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, workspace, li, lo, lg,
+                       dr, stream))
+    return st;
+  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, li, lo, lg, dr,
+                   stream);
 }
 
 }  // extern "C"

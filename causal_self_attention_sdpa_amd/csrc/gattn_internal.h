@@ -7,6 +7,8 @@
 #include <cstdint>
 #include <tuple>
 
+#include "philox.h"
+
 namespace gattn {
 
 // Launch a __global__ function through hipLaunchKernel so that the launch
@@ -100,39 +102,44 @@ inline size_t ws_part_bytes(int B, int H, int T) {
 // contiguous (B, H, T).
 // f32_fwd: Tq queries against Tk >= Tq keys, query i seeing keys
 // j <= Tk - Tq + i (Tq = Tk: the causal forward); q in layout lq, k and v in lk.
+// dr: dropout on the weights (dr.thr = 0: none), as in philox.h.
 hipError_t f32_fwd(const float* q, const float* k, const float* v, float* o, float* lse, int BH,
                    int H, int Tq, int Tk, int hs, float scale, Layout lq, Layout lk, Layout lo,
-                   hipStream_t s);
+                   const Dropout& dr, hipStream_t s);
 hipError_t f32_bwd_pre(const float* o, const float* dO, const float* lse, float* D, float* L2,
                        int BH, int H, int T, int hs, Layout lo, hipStream_t s);
 hipError_t f32_bwd_dkdv(const float* q, const float* k, const float* v, const float* dO,
                         const float* D, const float* L2, float* dk, float* dv, int BH, int H,
                         int T, int hs, float scale, Layout li, Layout lo, Layout lg,
-                        hipStream_t s);
+                        const Dropout& dr, hipStream_t s);
 hipError_t f32_bwd_dq(const float* q, const float* k, const float* v, const float* dO,
                       const float* lse, const float* D, float* dq, int BH, int H, int T, int hs,
-                      float scale, Layout li, Layout lo, Layout lg, hipStream_t s);
+                      float scale, Layout li, Layout lo, Layout lg, const Dropout& dr,
+                      hipStream_t s);
 
 // ---- 16-bit path: bf16 (f16 = false) or fp16 (f16 = true), hs in {32, 64}; MFMA ----
 hipError_t h16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                    float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
-                   bool f16, hipStream_t s);
+                   const Dropout& dr, bool f16, hipStream_t s);
 // Forward of the newest Tq tokens against Tk >= Tq keys, split over the key
 // range (partials in opart / lpart, then merged into o and lse).
 hipError_t h16_fwd_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                           float* lse, int BH, int H, int Tq, int Tk, int hs, float scale,
                           Layout lq, Layout lk, Layout lo, float* opart, float* lpart,
                           const DecodeSplit& ds, bool f16, hipStream_t s);
+// Keep decisions (bytes, 1 = kept) of every (b*H + h, i, j), j and i < T.
+hipError_t dropout_mask(uint8_t* keep, int BH, int T, const Dropout& dr, hipStream_t s);
 hipError_t h16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
                        float* L2, int BH, int H, int T, int hs, Layout lo, bool f16,
                        hipStream_t s);
 hipError_t h16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
                         uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
-                        Layout lo, Layout lg, bool f16, hipStream_t s);
+                        Layout lo, Layout lg, const Dropout& dr, bool f16, hipStream_t s);
 hipError_t h16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
                       float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
-                      Layout li, Layout lo, Layout lg, bool f16, hipStream_t s);
+                      Layout li, Layout lo, Layout lg, const Dropout& dr, bool f16,
+                      hipStream_t s);
 
 }  // namespace gattn

@@ -18,6 +18,12 @@
 // per-XCD L2s), the zeroing and conversion passes of an accumulator, and the
 // LDS round trip of dS; every output is deterministic.
 //
+// With dropout (DROP; mask Z = keep / (1 - p) on the weights, philox.h) the
+// forward computed O = (P*Z) V, and the chain rule gives
+//   dV = (P*Z)^T dO,   dP = Z * (dO V^T),   dS = P * (dP - D)
+// with the same D = rowsum(dO * O) (sum_j P Z (dO V^T) = dO . O).  The keep
+// decisions are recomputed from each weight's position, not stored.
+//
 // Both kernels stream tiles into double-buffered, swizzled LDS tiles by LDS
 // DMA (no register staging) with one barrier per step: the DMA for step t+1
 // runs while step t computes.  Tensors are addressed through Layout strides
@@ -29,6 +35,7 @@
 
 #include "mfma16_common.h"
 #include "gattn_internal.h"
+#include "philox.h"
 
 #ifndef GATTN_DKDV_STAGES
 #define GATTN_DKDV_STAGES 2
@@ -95,6 +102,14 @@ __global__ __launch_bounds__(kThreads) void pre16_kernel(const uint16_t* __restr
 //                                          transpose reads
 // In the steps that meet the diagonal, blocks wholly before this wavefront's
 // keys are skipped and the others masked.
+//
+// Dropout here sees a weight's keep decision in the transposed position: a
+// lane holds 8 consecutive queries of one key, while a generator block
+// covers 8 consecutive keys of one query.  The 8 lanes n = 8a .. 8a+7 (same
+// h) hold keys 8G .. 8G+7 against the same 8 queries I0 .. I0+7, so lane
+// 8a + r draws the block of query I0 + r, and the 8 blocks' keep bytes are
+// exchanged among the 8 lanes (xor 1, 2, 4); the lane then reads bit r of
+// byte e for query I0 + e.
 template <int HS>
 struct DkdvCfg {
   static constexpr int NW = 4;
@@ -118,7 +133,7 @@ struct DkdvRegs {
 
 // A(b): S and dP of query block qb.
 template <class E, int HS>
-__device__ inline void dkdv_sdp(const uint16_t* Qb, const uint16_t* Gb, int qb,
+__device__ __forceinline__ void dkdv_sdp(const uint16_t* Qb, const uint16_t* Gb, int qb,
                                 const LaneOffsets<HS>& L, const DkdvRegs<HS>& R, f32x16& s,
                                 f32x16& dp) {
   using C = DkdvCfg<HS>;
@@ -131,12 +146,45 @@ __device__ inline void dkdv_sdp(const uint16_t* Qb, const uint16_t* Gb, int qb,
   }
 }
 
-// B(b) then C(b) for query block qb.
-template <class E, int HS, bool MASK>
-__device__ inline void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
+// Lane xor M within each group of 32 lanes (ds_swizzle, bit-mask mode).
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_ds_swizzle(int(x), (M << 10) | 0x1F));
+}
+
+// The keep bytes of the 8 lanes 8a .. 8a+7 (lane 8a + r passes `byte`, r =
+// lane & 7): byte e of (lo, hi) as one 64-bit word is lane 8a + e's byte.
+__device__ __forceinline__ void gather8(uint32_t byte, int r, uint32_t& lo, uint32_t& hi) {
+  const uint32_t p1 = xor_lane<1>(byte);
+  const uint32_t x16 = (r & 1) ? (p1 | (byte << 8)) : (byte | (p1 << 8));
+  const uint32_t p2 = xor_lane<2>(x16);
+  const uint32_t x32 = (r & 2) ? (p2 | (x16 << 16)) : (x16 | (p2 << 16));
+  const uint32_t p4 = xor_lane<4>(x32);
+  lo = (r & 4) ? p4 : x32;
+  hi = (r & 4) ? x32 : p4;
+}
+
+// Keep bits of this lane's two runs of 8 queries in query block qb (run t:
+// queries qs0 + 32 qb + 16 t + 8h + e): bit 8e of w[t][0] (e < 4) or of
+// w[t][1] (e >= 4) is the decision for query e of the run and key krow.
+__device__ __forceinline__ void dkdv_keep(int qs0, int qb, int krow, int h, uint32_t bh,
+                                          const Dropout& dr, uint32_t (&w)[2][2]) {
+  const int r = krow & 7;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int q = qs0 + qb * 32 + 16 * t + 8 * h + r;
+    gather8(keep_bits8(uint32_t(q), uint32_t(krow) >> 3, bh, dr), r, w[t][0], w[t][1]);
+    w[t][0] >>= r;
+    w[t][1] >>= r;
+  }
+}
+
+// B(b) then C(b) for query block qb; w: its keep bits (DROP).
+template <class E, int HS, bool MASK, bool DROP>
+__device__ __forceinline__ void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
                                  const float* Db, int qb, int qs0, int krow, int h, float c,
                                  const LaneOffsets<HS>& L, const f32x16& s, const f32x16& dp,
-                                 DkdvRegs<HS>& R) {
+                                 DkdvRegs<HS>& R, const uint32_t (&w)[2][2], float zs) {
   using C = DkdvCfg<HS>;
   u32x4 pp[2], dsp[2];
 #pragma unroll
@@ -153,8 +201,14 @@ __device__ inline void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const f
       const float De = e < 4 ? d0[e] : d1[e - 4];
       float p = __builtin_amdgcn_exp2f(fmaf(s[8 * t + e], c, -le));
       if (MASK && krow > qs0 + ql + e) p = 0.f;
-      pv[e] = p;
-      dsv[e] = p * (dp[8 * t + e] - De);
+      if constexpr (DROP) {
+        const uint32_t wb = w[t][e >> 2];
+        pv[e] = keep_or_zero(p, wb, 8 * (e & 3));
+        dsv[e] = p * (keep_or_zero(dp[8 * t + e] * zs, wb, 8 * (e & 3)) - De);
+      } else {
+        pv[e] = p;
+        dsv[e] = p * (dp[8 * t + e] - De);
+      }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -173,45 +227,51 @@ __device__ inline void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const f
 }
 
 // One step below the diagonal: every block is visible, no mask.
-template <class E, int HS>
-__device__ inline void dkdv_step_full(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
+template <class E, int HS, bool DROP>
+__device__ __forceinline__ void dkdv_step_full(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
                                       const float* Db, int qs0, int krow, int h, float c,
-                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R) {
+                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R, uint32_t bh,
+                                      const Dropout& dr) {
   using C = DkdvCfg<HS>;
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
+    uint32_t w[2][2] = {};
+    if constexpr (DROP) dkdv_keep(qs0, qb, krow, h, bh, dr, w);
     f32x16 s, dp;
     dkdv_sdp<E, HS>(Qb, Gb, qb, L, R, s, dp);
-    dkdv_grad<E, HS, false>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R);
+    dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R, w, dr.zs);
   }
 }
 
 // A step that meets the diagonal: blocks wholly before this wavefront's keys
 // are skipped, the others masked.
-template <class E, int HS>
-__device__ inline void dkdv_step_diag(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
+template <class E, int HS, bool DROP>
+__device__ __forceinline__ void dkdv_step_diag(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
                                       const float* Db, int qs0, int kw0, int krow, int h, float c,
-                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R) {
+                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R, uint32_t bh,
+                                      const Dropout& dr) {
   using C = DkdvCfg<HS>;
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     if (kw0 > qs0 + qb * 32 + 31) continue;  // all of this wavefront's keys lie after the block
+    uint32_t w[2][2] = {};
+    if constexpr (DROP) dkdv_keep(qs0, qb, krow, h, bh, dr, w);
     f32x16 s, dp;
     dkdv_sdp<E, HS>(Qb, Gb, qb, L, R, s, dp);
-    dkdv_grad<E, HS, true>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R);
+    dkdv_grad<E, HS, true, DROP>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R, w, dr.zs);
   }
 }
 
 // STRIDED = false: every tensor is contiguous (B, H, T, hs) and the row
 // strides are the compile-time HS (the strides' registers and multiplies
-// would otherwise push this kernel into spills).
-template <class E, int HS, bool STRIDED>
+// would otherwise push this kernel into spills).  DROP: dropout with dr.
+template <class E, int HS, bool STRIDED, bool DROP>
 __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void dkdv16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
     const float* __restrict__ Dg, const float* __restrict__ L2g, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int BH, int H, int T, float scale, Layout li, Layout lo,
-    Layout lg) {
+    Layout lg, Dropout dr) {
   using C = DkdvCfg<HS>;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[C::NS][C::BQ * HS];
   __shared__ __attribute__((aligned(16))) uint16_t Gs[C::NS][C::BQ * HS];
@@ -273,9 +333,11 @@ __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void dkdv16_kernel(
     if (t + C::NS - 1 < nsteps) issue(qt0 + t + C::NS - 1, (buf + C::NS - 1) % C::NS);
     const int qs0 = (qt0 + t) * C::BQ;
     if (qs0 < k0 + C::BN)
-      dkdv_step_diag<E, HS>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, kw0, krow, h, c, L, R);
+      dkdv_step_diag<E, HS, DROP>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, kw0, krow, h, c, L, R,
+                                  uint32_t(bh), dr);
     else
-      dkdv_step_full<E, HS>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, krow, h, c, L, R);
+      dkdv_step_full<E, HS, DROP>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, krow, h, c, L, R,
+                                  uint32_t(bh), dr);
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nsteps - t - 2)));
     __syncthreads();
   };
@@ -286,13 +348,14 @@ __global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void dkdv16_kernel(
   const uint32_t gbytes = slice_bytes_of<HS, STRIDED>(lg, T);
   const rsrc_t wk = make_rsrc(dk + gbase, gbytes), wv = make_rsrc(dv + gbase, gbytes);
   const int rsg = STRIDED ? int(lg.st) : HS;
+  const float zv = DROP ? dr.zs : 1.f;  // dV = (P*Z)^T dO: the kept weights' factor
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t off = uint32_t(krow * rsg + db * 32 + 8 * g + 4 * h) * 2;
-      bstore8(wv, off, u32x2{E::pack(R.dva[db][4 * g], R.dva[db][4 * g + 1]),
-                             E::pack(R.dva[db][4 * g + 2], R.dva[db][4 * g + 3])});
+      bstore8(wv, off, u32x2{E::pack(R.dva[db][4 * g] * zv, R.dva[db][4 * g + 1] * zv),
+                             E::pack(R.dva[db][4 * g + 2] * zv, R.dva[db][4 * g + 3] * zv)});
       bstore8(wk, off, u32x2{E::pack(R.dka[db][4 * g] * scale, R.dka[db][4 * g + 1] * scale),
                              E::pack(R.dka[db][4 * g + 2] * scale, R.dka[db][4 * g + 3] * scale)});
     }
@@ -328,14 +391,17 @@ struct DqCfg {
 // 32 lie after every query (skipped); kDiagHi, key0 + 32 == q0: the second
 // 32 keys form the diagonal block.  In the diagonal block register 8t+e of
 // lane (n, h) holds key (q0 + 16t + 8h + e), after query q0 + n exactly when
-// 16t + e > dn = n - 8h.
+// 16t + e > dn = n - 8h.  With DROP, registers 8t..8t+7 of block kb are keys
+// 8 * (g0 + 4 kb + 2 t) .. +7 of query qrow (g0 = key0 / 8 + h): one generator
+// block, as in the forward.
 enum DqTile { kFull = 0, kDiagLo = 1, kDiagHi = 2 };
 
-template <class E, int HS, int KIND>
+template <class E, int HS, int KIND, bool DROP>
 __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, int dn, float c,
                                         float lse2, float Dq, const LaneOffsets<HS>& L,
                                         const u32x4 (&qf)[HS / 16], const u32x4 (&gf)[HS / 16],
-                                        f32x16 (&dqa)[HS / 32]) {
+                                        f32x16 (&dqa)[HS / 32], uint32_t qrow, uint32_t g0,
+                                        uint32_t bh, const Dropout& dr) {
   using C = DqCfg<HS>;
   constexpr int NKB = KIND == kDiagLo ? 1 : 2;  // 32-key blocks computed
   constexpr int KD = KIND == kDiagLo ? 0 : (KIND == kDiagHi ? 1 : -1);  // the diagonal block
@@ -350,12 +416,17 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      uint32_t bits = 0xFFu;
+      if constexpr (DROP) bits = keep_bits8(qrow, g0 + 4 * kb + 2 * t, bh, dr);
       float dsv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float p = __builtin_amdgcn_exp2f(fmaf(st[8 * t + e], c, -lse2));
         if (kb == KD && 16 * t + e > dn) p = 0.f;
-        dsv[e] = p * (dpt[8 * t + e] - Dq);
+        if constexpr (DROP)
+          dsv[e] = p * (keep_or_zero(dpt[8 * t + e] * dr.zs, bits, e) - Dq);
+        else
+          dsv[e] = p * (dpt[8 * t + e] - Dq);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) dsp[kb][t][e] = E::pack(dsv[2 * e], dsv[2 * e + 1]);
@@ -378,13 +449,13 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
   }
 }
 
-template <class E, int HS, bool STRIDED>  // STRIDED as for the dK/dV kernel
+template <class E, int HS, bool STRIDED, bool DROP>  // STRIDED, DROP as for the dK/dV kernel
 __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void dq16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, float* __restrict__ Dg,
     float* __restrict__ L2g, uint16_t* __restrict__ dq, int BH, int H, int T, float scale,
-    Layout li, Layout lo, Layout lg) {
+    Layout li, Layout lo, Layout lg, Dropout dr) {
   using C = DqCfg<HS>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[C::NS][C::BN * HS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[C::NS][C::BN * HS];
@@ -455,13 +526,17 @@ __global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void dq16_kernel(
     constexpr int buf = decltype(bufc)::value;
     if (kt + C::NS - 1 < nkt) issue(kt + C::NS - 1, (buf + C::NS - 1) % C::NS);
     const int key0 = kt * C::BN;
+    const uint32_t g0 = uint32_t(key0 / 8 + h), ub = uint32_t(bh), uq = uint32_t(qrow);
     if (q0 < T && key0 <= q0) {
       if (key0 == q0)
-        dq_step<E, HS, kDiagLo>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
+        dq_step<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, uq, g0,
+                                      ub, dr);
       else if (key0 + 32 == q0)
-        dq_step<E, HS, kDiagHi>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
+        dq_step<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, uq, g0,
+                                      ub, dr);
       else
-        dq_step<E, HS, kFull>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa);
+        dq_step<E, HS, kFull, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, uq, g0, ub,
+                                    dr);
     }
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
@@ -499,28 +574,36 @@ template <class E>
 hipError_t dkdv16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
                          uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
-                         Layout lo, Layout lg, hipStream_t s) {
+                         Layout lo, Layout lg, const Dropout& dr, hipStream_t s) {
   const int bn = DkdvCfg<64>::BN;
   const dim3 grid(unsigned(((T + bn - 1) / bn) * BH));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
-  auto kern = hs == 64 ? (strided ? dkdv16_kernel<E, 64, true> : dkdv16_kernel<E, 64, false>)
-                       : (strided ? dkdv16_kernel<E, 32, true> : dkdv16_kernel<E, 32, false>);
+  auto pick = [&](auto dropc) {
+    constexpr bool D = decltype(dropc)::value;
+    return hs == 64 ? (strided ? dkdv16_kernel<E, 64, true, D> : dkdv16_kernel<E, 64, false, D>)
+                    : (strided ? dkdv16_kernel<E, 32, true, D> : dkdv16_kernel<E, 32, false, D>);
+  };
+  auto kern = dr.thr != 0 ? pick(std::true_type{}) : pick(std::false_type{});
   return launch(kern, grid, dim3(kThreads), s, q, k, v, dO, D, L2, dk, dv, BH, H, T, scale, li, lo,
-                lg);
+                lg, dr);
 }
 
 template <class E>
 hipError_t dq16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
                        float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
-                       Layout li, Layout lo, Layout lg, hipStream_t s) {
+                       Layout li, Layout lo, Layout lg, const Dropout& dr, hipStream_t s) {
   const int bm = DqCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
-  auto kern = hs == 64 ? (strided ? dq16_kernel<E, 64, true> : dq16_kernel<E, 64, false>)
-                       : (strided ? dq16_kernel<E, 32, true> : dq16_kernel<E, 32, false>);
+  auto pick = [&](auto dropc) {
+    constexpr bool D = decltype(dropc)::value;
+    return hs == 64 ? (strided ? dq16_kernel<E, 64, true, D> : dq16_kernel<E, 64, false, D>)
+                    : (strided ? dq16_kernel<E, 32, true, D> : dq16_kernel<E, 32, false, D>);
+  };
+  auto kern = dr.thr != 0 ? pick(std::true_type{}) : pick(std::false_type{});
   return launch(kern, grid, dim3(kThreads), s, q, k, v, o, dO, lse, D, L2, dq, BH, H, T, scale, li,
-                lo, lg);
+                lo, lg, dr);
 }
 }  // namespace
 
@@ -534,19 +617,20 @@ hipError_t h16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, 
 hipError_t h16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
                         uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
-                        Layout lo, Layout lg, bool f16, hipStream_t s) {
+                        Layout lo, Layout lg, const Dropout& dr, bool f16, hipStream_t s) {
   if (f16)
-    return dkdv16_launch<F16>(q, k, v, dO, D, L2, dk, dv, BH, H, T, hs, scale, li, lo, lg, s);
-  return dkdv16_launch<Bf16>(q, k, v, dO, D, L2, dk, dv, BH, H, T, hs, scale, li, lo, lg, s);
+    return dkdv16_launch<F16>(q, k, v, dO, D, L2, dk, dv, BH, H, T, hs, scale, li, lo, lg, dr, s);
+  return dkdv16_launch<Bf16>(q, k, v, dO, D, L2, dk, dv, BH, H, T, hs, scale, li, lo, lg, dr, s);
 }
 
 hipError_t h16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
                       float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
-                      Layout li, Layout lo, Layout lg, bool f16, hipStream_t s) {
+                      Layout li, Layout lo, Layout lg, const Dropout& dr, bool f16,
+                      hipStream_t s) {
   if (f16)
-    return dq16_launch<F16>(q, k, v, o, dO, lse, D, L2, dq, BH, H, T, hs, scale, li, lo, lg, s);
-  return dq16_launch<Bf16>(q, k, v, o, dO, lse, D, L2, dq, BH, H, T, hs, scale, li, lo, lg, s);
+    return dq16_launch<F16>(q, k, v, o, dO, lse, D, L2, dq, BH, H, T, hs, scale, li, lo, lg, dr, s);
+  return dq16_launch<Bf16>(q, k, v, o, dO, lse, D, L2, dq, BH, H, T, hs, scale, li, lo, lg, dr, s);
 }
 
 }  // namespace gattn

@@ -26,6 +26,11 @@
 //                                   accumulators (no LDS round trip), V^T
 //                                   read from the row-major V tile with LDS
 //                                   transpose reads.
+// With dropout (DROP), each weight's keep decision comes from the counter-
+// based generator of philox.h: the lane's run of 8 consecutive keys of one
+// query is exactly one generator block.  The row sum l takes the weights
+// before dropout (the softmax is normalised first), the value sum only the
+// kept ones, and the output is multiplied by 1/(1 - p) with 1/l.
 // Tensors are addressed through Layout strides (q, k, v: li; o: lo), so the
 // fused (B, T, 3C) projection output and a (B, T, C) output are read and
 // written in place.  Rows past T are read as zeros (buffer resources sized to
@@ -36,6 +41,7 @@
 
 #include "mfma16_common.h"
 #include "gattn_internal.h"
+#include "philox.h"
 
 #ifndef GATTN_FWD_STAGES
 #define GATTN_FWD_STAGES 2
@@ -75,11 +81,14 @@ enum TileKind { kFull = 0, kDiagLo = 1, kDiagHi = 2 };
 
 // One key tile for one wavefront.  `dn` = n - 8h: in the diagonal block,
 // register i of lane (n, h) holds key (q0 + 16*(i/8) + 8h + i%8), which lies
-// above query q0 + n exactly when 16*(i/8) + i%8 > dn.
-template <class E, int HS, int KIND>
+// above query q0 + n exactly when 16*(i/8) + i%8 > dn.  With DROP, the run of
+// registers 8t..8t+7 of half kh is keys 8 * (g0 + 4 kh + 2 t) .. +7 of query
+// qrow (g0 = key0 / 8 + h).
+template <class E, int HS, int KIND, bool DROP>
 __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb, int dn, float c,
                                          const LaneOffsets<HS>& L, const u32x4 (&qf)[HS / 16],
-                                         FwdState<HS>& st) {
+                                         FwdState<HS>& st, uint32_t qrow, uint32_t g0,
+                                         uint32_t bh, const Dropout& dr) {
   using C = FwdCfg<HS>;
   constexpr int NKH = KIND == kDiagLo ? 1 : 2;  // 32-key halves computed
   f32x16 s[2];
@@ -123,14 +132,20 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb,
 #pragma unroll
   for (int kh = 0; kh < NKH; ++kh)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      uint32_t bits = 0xFFu;
+      if constexpr (DROP) bits = keep_bits8(qrow, g0 + 4 * kh + 2 * t, bh, dr);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e], c, -mc));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e + 1], c, -mc));
-        pf[kh][t][e] = E::pack(p0, p1);
+        if constexpr (DROP)
+          pf[kh][t][e] = E::pack(keep_or_zero(p0, bits, 2 * e), keep_or_zero(p1, bits, 2 * e + 1));
+        else
+          pf[kh][t][e] = E::pack(p0, p1);
         st.l += p0 + p1;
       }
+    }
 #pragma unroll
   for (int kh = 0; kh < NKH; ++kh)
 #pragma unroll
@@ -141,15 +156,15 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb,
 }
 
 // STRIDED = false: q, k, v and o are contiguous (B, H, T, hs) and the row
-// strides are the compile-time HS.
-template <class E, int HS, bool STRIDED>
+// strides are the compile-time HS.  DROP: dropout with the parameters dr.
+template <class E, int HS, bool STRIDED, bool DROP>
 __global__ __launch_bounds__(kThreads) void fwd16_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
                                                            uint16_t* __restrict__ o,
                                                            float* __restrict__ lse, int BH, int H,
                                                            int T, float scale, Layout li,
-                                                           Layout lo) {
+                                                           Layout lo, Dropout dr) {
   using C = FwdCfg<HS>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[C::NS][C::BN * HS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[C::NS][C::BN * HS];
@@ -202,13 +217,14 @@ __global__ __launch_bounds__(kThreads) void fwd16_kernel(const uint16_t* __restr
     constexpr int buf = decltype(bufc)::value;
     if (kt + C::NS - 1 < nkt) issue(kt + C::NS - 1, (buf + C::NS - 1) % C::NS);
     const int key0 = kt * C::BN;
+    const uint32_t g0 = uint32_t(key0 / 8 + h);
     if (q0 < T && key0 <= q0) {  // this wavefront sees some key of the tile
       if (key0 == q0)
-        fwd_tile<E, HS, kDiagLo>(Ks[buf], Vs[buf], dn, c, L, qf, st);
+        fwd_tile<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], dn, c, L, qf, st, qrow, g0, bh, dr);
       else if (key0 + 32 == q0)
-        fwd_tile<E, HS, kDiagHi>(Ks[buf], Vs[buf], dn, c, L, qf, st);
+        fwd_tile<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], dn, c, L, qf, st, qrow, g0, bh, dr);
       else
-        fwd_tile<E, HS, kFull>(Ks[buf], Vs[buf], dn, c, L, qf, st);
+        fwd_tile<E, HS, kFull, DROP>(Ks[buf], Vs[buf], dn, c, L, qf, st, qrow, g0, bh, dr);
     }
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
@@ -219,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void fwd16_kernel(const uint16_t* __restr
   // l > 0 for every real row.  O^T register i of lane (n, h): column
   // d = db*32 + 8*(i/4) + 4h + i%4 of row qrow.
   const float lt = halves_sum(st.l);
-  const float inv = 1.f / lt;
+  const float inv = (DROP ? dr.zs : 1.f) / lt;
   const rsrc_t wo = make_rsrc(o + slice_base<HS, STRIDED>(lo, bh, H, T),
                               slice_bytes_of<HS, STRIDED>(lo, T));
   const int rso = STRIDED ? int(lo.st) : HS;
@@ -242,21 +258,25 @@ namespace {
 template <class E>
 hipError_t fwd16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                         float* lse, int BH, int H, int T, int hs, float scale, Layout li,
-                        Layout lo, hipStream_t s) {
+                        Layout lo, const Dropout& dr, hipStream_t s) {
   const int bm = FwdCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lo);
-  auto kern = hs == 64 ? (strided ? fwd16_kernel<E, 64, true> : fwd16_kernel<E, 64, false>)
-                       : (strided ? fwd16_kernel<E, 32, true> : fwd16_kernel<E, 32, false>);
-  return launch(kern, grid, dim3(kThreads), s, q, k, v, o, lse, BH, H, T, scale, li, lo);
+  auto pick = [&](auto dropc) {
+    constexpr bool D = decltype(dropc)::value;
+    return hs == 64 ? (strided ? fwd16_kernel<E, 64, true, D> : fwd16_kernel<E, 64, false, D>)
+                    : (strided ? fwd16_kernel<E, 32, true, D> : fwd16_kernel<E, 32, false, D>);
+  };
+  auto kern = dr.thr != 0 ? pick(std::true_type{}) : pick(std::false_type{});
+  return launch(kern, grid, dim3(kThreads), s, q, k, v, o, lse, BH, H, T, scale, li, lo, dr);
 }
 }  // namespace
 
 hipError_t h16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                    float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
-                   bool f16, hipStream_t s) {
-  if (f16) return fwd16_launch<F16>(q, k, v, o, lse, BH, H, T, hs, scale, li, lo, s);
-  return fwd16_launch<Bf16>(q, k, v, o, lse, BH, H, T, hs, scale, li, lo, s);
+                   const Dropout& dr, bool f16, hipStream_t s) {
+  if (f16) return fwd16_launch<F16>(q, k, v, o, lse, BH, H, T, hs, scale, li, lo, dr, s);
+  return fwd16_launch<Bf16>(q, k, v, o, lse, BH, H, T, hs, scale, li, lo, dr, s);
 }
 
 }  // namespace gattn

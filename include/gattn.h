@@ -209,6 +209,58 @@ int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, 
                    void* dv, int B, int H, int T, int hs, float scale, int dtype, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Attention dropout.  The RobGPT page ("GPT da zero", parameter table) trains
+ * with dropout 0.1; the GPT-2 124M configuration ("Model Architecture
+ * Nanogpt", Workflow 2) uses 0.0.  Dropout acts on the attention weights after
+ * the row softmax and before the value sum, with kept weights scaled by
+ * 1/(1 - p):
+ *   O[i][:] = sum_j P[i][j] * Z[i][j] * V[j][:],   Z = keep / (1 - p_eff),
+ * lse is that of the softmax before dropout, and the backward is
+ *   dV = (P*Z)^T dO,   dS = P * (Z * (dO V^T) - D),   D[i] = dO[i] . O[i],
+ *   dQ = scale dS K,   dK = scale dS^T Q.
+ * Mask: t = floor(p * 65536 + 0.5) (p as given, in double precision; the
+ * effective probability is p_eff = t / 65536).  For slice (b, h), query i,
+ * key j, the Philox-4x32-10 generator (Salmon, Moraes, Dror, Shaw, SC 2011)
+ * with counter (i, j >> 3, b*H + h, offset) and key (seed mod 2^32,
+ * seed >> 32) gives four 32-bit words; u(i, j) is the (j & 1)-th 16-bit half
+ * (low half first) of word (j & 7) >> 1, and keep(i, j) = u(i, j) >= t.  The
+ * same (seed, offset) draws the same mask in the forward, the backward and
+ * gattn_dropout_mask; give each layer and step its own (seed, offset).
+ * The mask is recomputed where needed, never stored.
+ *
+ * gattn_fwd_dropout: as gattn_fwd_strided (strides NULL = contiguous) with
+ * dropout of probability p.  p = 0 (t = 0) runs exactly gattn_fwd_strided.
+ * INVALID_ARG also for p not finite, p < 0, p >= 1, or t > 65535.
+ */
+int gattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int H, int T, int hs, float scale, int dtype, float p,
+                      uint64_t seed, uint32_t offset, const int64_t* qkv_strides,
+                      const int64_t* o_strides, hipStream_t stream);
+
+/*
+ * gattn_bwd_dropout: the backward of gattn_fwd_dropout with the same p, seed
+ * and offset (o and lse as that forward wrote them); arguments, workspace and
+ * strides as gattn_bwd_strided.  p = 0 runs exactly gattn_bwd_strided.
+ */
+int gattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int T, int hs,
+                      float scale, int dtype, float p, uint64_t seed, uint32_t offset,
+                      void* workspace, size_t workspace_bytes, const int64_t* qkv_strides,
+                      const int64_t* o_strides, const int64_t* grad_strides,
+                      hipStream_t stream);
+
+/*
+ * gattn_dropout_mask: the keep decisions of the mask above as bytes
+ * (1 = kept, 0 = dropped), keep[((b*H + h) * T + i) * T + j] for every i, j < T
+ * (above the causal diagonal too), from the same generator code the kernels
+ * use.  keep: device buffer of B*H*T*T bytes (no alignment needed).
+ * INVALID_ARG for keep NULL, B, H or T < 1, B*H*T*T >= 2^40, or p as in
+ * gattn_fwd_dropout.
+ */
+int gattn_dropout_mask(uint8_t* keep, int B, int H, int T, float p, uint64_t seed,
+                       uint32_t offset, hipStream_t stream);
+
 /* Static, human-readable name of a gattn_status value. */
 const char* gattn_status_string(int status);
 

@@ -84,7 +84,8 @@ U_BF16 = 2.0 ** -8  # unit roundoff of bfloat16 (8 significant bits)
 U_F16 = 2.0 ** -11  # unit roundoff of IEEE binary16 (11 significant bits)
 
 
-def rounding_bound(x: dict, scale: float, slices, ref, u: float = U_BF16, slack: float = 1e-3):
+def rounding_bound(x: dict, scale: float, slices, ref, u: float = U_BF16, slack: float = 1e-3,
+                   z=None):
     """First-order bound on the error of a 16-bit path, per element, for the
     selected (b, h) slices, derived from where that path rounds:
       o  = P V           P rounded to bf16 before the MFMA
@@ -96,21 +97,24 @@ def rounding_bound(x: dict, scale: float, slices, ref, u: float = U_BF16, slack:
     |err| <= u (|ref| + Mag) + slack with Mag = sum of |operand products|; u
     is the unit roundoff of the 16-bit type (bf16 2^-8, fp16 2^-11), `slack`
     covers the float32 arithmetic (and is the whole bound of lse, which is
-    never rounded to 16 bits)."""
+    never rounded to 16 bits).  With attention dropout, z (n, T, T) holds the
+    weight multipliers of each selected slice: P Z takes P's place in o and
+    dv, and dS = P (Z dP - D)."""
     sel = {n: np.stack([a[b, h] for b, h in slices]) for n, a in x.items()}
     dq_r, dk_r, dv_r, o_r, lse_r = (a[:, 0] for a in ref)
     T = sel["q"].shape[1]
     causal = np.tril(np.ones((T, T), dtype=bool))
     s = np.einsum("nid,njd->nij", sel["q"], sel["k"]) * scale
     P = np.where(causal, np.exp(np.where(causal, s, 0.0) - lse_r[:, :, None]), 0.0)
+    Z = np.ones_like(P) if z is None else np.asarray(z, dtype=np.float64)
     A = np.sum(np.abs(sel["do"]) * np.abs(o_r), axis=-1)          # |dO|.|O| per row
     D = np.sum(sel["do"] * o_r, axis=-1)
     dP = np.einsum("nid,njd->nij", sel["do"], sel["v"])
-    dS = P * (dP - D[:, :, None])
+    dS = P * (Z * dP - D[:, :, None])
     W = np.abs(dS) + P * A[:, :, None]
     mag = {
-        "o": P @ np.abs(sel["v"]),
-        "dv": np.swapaxes(P, 1, 2) @ np.abs(sel["do"]),
+        "o": (P * Z) @ np.abs(sel["v"]),
+        "dv": np.swapaxes(P * Z, 1, 2) @ np.abs(sel["do"]),
         "dk": scale * np.swapaxes(W, 1, 2) @ np.abs(sel["q"]),
         "dq": scale * W @ np.abs(sel["k"]),
     }

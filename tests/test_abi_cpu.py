@@ -214,3 +214,32 @@ def test_decode_validation(lib):
     assert ga.gattn_fwd_decode_workspace_bytes(2, 3, 1, 256, 64, 1) == 0   # 4 tiles: no split
     assert ga.gattn_fwd_decode_workspace_bytes(2, 3, 5, 4, 64, 1) == 0     # Tq > Tk rejected
     assert ga.gattn_fwd_decode_workspace_bytes(2, 3, 1, 100, 48, 1) == 0   # unsupported hs
+
+
+def test_dropout_validation(lib):
+    def fwd(p=0.1, q=P, o=P, lse=P, hs=64, dtype=1, sqkv=None, so=None):
+        return lib.gattn_fwd_dropout(q, P, P, o, lse, 2, 3, 100, hs, 0.125, dtype, p, 7, 1, sqkv,
+                                     so, None)
+
+    def bwd(p=0.1, lse=P, ws=P, wsb=1 << 20, dtype=1, sg=None):
+        return lib.gattn_bwd_dropout(P, P, P, P, P, lse, P, P, P, 2, 3, 100, 64, 0.125, dtype, p, 7,
+                                     1, ws, wsb, None, None, sg, None)
+
+    def mask(keep=P, B=2, H=3, T=100, p=0.1):
+        return lib.gattn_dropout_mask(keep, B, H, T, p, 7, 1, None)
+
+    for bad in (-0.1, 1.0, 2.0, float("nan"), float("inf"), 1.0 - 2.0 ** -18):
+        assert fwd(p=bad) == INVALID, bad
+        assert bwd(p=bad) == INVALID, bad
+        assert mask(p=bad) == INVALID, bad
+    assert fwd(q=None) == INVALID
+    assert fwd(lse=P + 4) == INVALID
+    assert fwd(hs=48) == UNSUPPORTED
+    assert fwd(so=_st(3 * 100 * 64, 100 * 64, 8)) == INVALID  # row stride < hs
+    assert bwd(lse=None) == INVALID                              # the backward needs lse
+    assert bwd(ws=None) == WORKSPACE
+    assert bwd(wsb=16) == WORKSPACE
+    assert bwd(sg=_st(-1, 64, 64)) == INVALID
+    assert mask(keep=None) == INVALID
+    assert mask(T=0) == INVALID
+    assert mask(B=1 << 10, H=1 << 10, T=1 << 10) == INVALID     # 2^40 bytes
