@@ -68,9 +68,16 @@ CSRC = os.path.join(ROOT, "causal_self_attention_sdpa_amd", "csrc")
 #          algorithmic bytes per launch in units of one (B,H,T,hs) bf16 tensor, and of one
 #          (B,H,T) fp32 row vector)
 KERNELS = {
-    "fwd": ("fwd16_kernel<{E}, {hs}, false>", "mfma16_fwd.hip", 4, 4, 1),  # q k v in; o, lse out
-    "dq": ("dq16_kernel<{E}, {hs}, false>", "mfma16_bwd.hip", 2, 6, 1),  # q k v o dO lse in; dq out
-    "dkdv": ("dkdv16_kernel<{E}, {hs}, false>", "mfma16_bwd.hip", 6, 6, 0),  # q k v dO in; dk dv out
+    "fwd": ("fwd16_kernel<{E}, {hs}, false, false>", "mfma16_fwd.hip", 4, 4, 1),  # q k v in; o, lse out
+    "dq": ("dq16_kernel<{E}, {hs}, false, false>", "mfma16_bwd.hip", 2, 6, 1),  # q k v o dO lse in; dq out
+    "dkdv": ("dkdv16_kernel<{E}, {hs}, false, false>", "mfma16_bwd.hip", 6, 6, 0),  # q k v dO in; dk dv out
+}
+# With attention dropout (--dropout): the forward kernel, and the backward as
+# one call (its dQ and dK/dV kernels back to back), timed as one unit.
+DROP_KERNELS = {
+    "fwd_dropout": ("fwd16_kernel<{E}, {hs}, false, true>", "mfma16_fwd.hip", 4, 4, 1),
+    "bwd_dropout": ("dq16_kernel<{E}, {hs}, false, true> + dkdv16_kernel<{E}, {hs}, false, true>",
+                    "mfma16_bwd.hip", 8, 8, 1),  # q k v o dO lse in; dq dk dv out
 }
 
 
@@ -124,15 +131,17 @@ def read_traffic(name: str, tag: str):
     text = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != source_digest(os.path.join(CSRC, KERNELS[name][1])):
+    src = {**KERNELS, **DROP_KERNELS}[name][1]
+    if not m or not t or m.group(1) != source_digest(os.path.join(CSRC, src)):
         return None
     return float(t.group(1))
 
 
-def cpu_baseline(host_layers, scale, nslices: int):
+def cpu_baseline(host_layers, scale, nslices: int, dropout: float = 0.0):
     """The CPU oracle (as it stands) on the first `nslices` (layer, b, h)
     slices of the workload, all host threads of this process's CPU share (at
-    most 16)."""
+    most 16).  With dropout, the oracle's dropout path (numpy, one thread per
+    its BLAS) on the same slices with the bench's seed and per-layer offsets."""
     import numpy as np
 
     import oracle
@@ -144,14 +153,25 @@ def cpu_baseline(host_layers, scale, nslices: int):
            for n in ("q", "k", "v", "do")}
     threads = min(16, len(os.sched_getaffinity(0)))
     t0 = time.perf_counter()
-    oracle.attention_backward(sel["q"], sel["k"], sel["v"], sel["do"], scale, nthreads=threads)
+    if dropout > 0.0:
+        from oracle import dropout as od
+        for l in sorted({l for l, _, _ in idx}):
+            sl = [(b, h) for ll, b, h in idx if ll == l]
+            x = host_layers[l]
+            od.attention_backward_dropout(x["q"], x["k"], x["v"], x["do"], scale, dropout, 0x5EED,
+                                          l, slices=sl)
+        threads = int(os.environ.get("OMP_NUM_THREADS", threads))
+    else:
+        oracle.attention_backward(sel["q"], sel["k"], sel["v"], sel["do"], scale,
+                                  nthreads=threads)
     dt = time.perf_counter() - t0
     ff, fb = flops(len(idx), 1, T, hs)
     nl = idx[-1][0] + 1
     return {"value": round((ff + fb) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"{len(idx)} of the {B * H * len(host_layers)} (layer,b,h) slices "
-                      f"(layers 0..{nl - 1}; T={T}, hs={hs}), forward+backward in float64, "
+                      f"(layers 0..{nl - 1}; T={T}, hs={hs}), forward+backward in float64"
+                      f"{f' with dropout p={dropout}' if dropout > 0 else ''}, "
                       f"FLOP counted as on the GPU"}
 
 
@@ -346,6 +366,9 @@ def main() -> int:
                          "dqkv (B,T,3C), through the strided entry points; copies: the "
                          "contiguous kernels plus the transposes a caller of the contiguous "
                          "entry points needs around them")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="attention dropout probability (train mode, contiguous layout); the "
+                         "mask is drawn per layer and step from a seed and an offset")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-slices", type=int, default=400,
@@ -409,7 +432,12 @@ def main() -> int:
                      device=dev)
     stream = torch.cuda.current_stream()
     timer = HipTimer()
-    ev = {k: [(timer.event(), timer.event()) for _ in range(args.steps)] for k in KERNELS}
+    drop = args.dropout > 0.0
+    if drop and args.layout != "contiguous":
+        print("--dropout is measured with the contiguous layout only", file=sys.stderr)
+        return 2
+    KT = DROP_KERNELS if drop else KERNELS
+    ev = {k: [(timer.event(), timer.event()) for _ in range(args.steps)] for k in KT}
     seq = [(timer.event(), timer.event(), timer.event()) for _ in range(args.steps)]
 
     # C-ABI argument tuples, marshalled once: the timed loop is nothing but
@@ -419,7 +447,20 @@ def main() -> int:
     p = lambda x: x.data_ptr()
     wsb = ws.numel()
     call = []
-    for t in layers:
+    for l, t in enumerate(layers):
+        if drop:
+            # seed fixed, offset = layer: each layer draws its own mask
+            pd, seed, off = args.dropout, 0x5EED, l
+            call.append({
+                "fwd_dropout": (lib.gattn_fwd_dropout,
+                                (p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["lse"]), B, H, T,
+                                 hs, scale, dcode, pd, seed, off, None, None, sp)),
+                "bwd_dropout": (lib.gattn_bwd_dropout,
+                                (p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["do"]),
+                                 p(t["lse"]), p(t["dq"]), p(t["dk"]), p(t["dv"]), B, H, T, hs,
+                                 scale, dcode, pd, seed, off, p(ws), wsb, None, None, None, sp)),
+            })
+            continue
         call.append({
             "fwd": (lib.gattn_fwd, (p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["lse"]),
                                     B, H, T, hs, scale, dcode, sp)),
@@ -509,11 +550,14 @@ def main() -> int:
         if record is not None:
             timer.record(seq[record][0], sp)
         for l in range(L):
-            run(l, "fwd", record if l == lt else None)
+            run(l, "fwd_dropout" if drop else "fwd", record if l == lt else None)
         if record is not None:
             timer.record(seq[record][1], sp)
         for l in reversed(range(L)):
             i = record if l == lt else None
+            if drop:
+                run(l, "bwd_dropout", i)
+                continue
             run(l, "dq", i)
             run(l, "dkdv", i)
         if record is not None:
@@ -555,18 +599,18 @@ def main() -> int:
         print(json.dumps(out), flush=True)
         return 0
     mean_us = {k: float(np.mean([timer.elapsed_ms(a, b) for a, b in ev[k]])) * 1e3
-               for k in KERNELS}
+               for k in KT}
     dom = max(mean_us, key=mean_us.get)
-    sym = KERNELS[dom][0].format(hs=hs, E="Bf16" if args.dtype == "bf16" else "F16")
+    sym = KT[dom][0].format(hs=hs, E="Bf16" if args.dtype == "bf16" else "F16")
     if W["bound"] == "mfma":
-        alg = KERNELS[dom][2] * hs * pairs
+        alg = KT[dom][2] * hs * pairs
         achieved = alg / (mean_us[dom] * 1e-6) / 1e12
         roof = {"kernel": sym, "bound": "mfma", "achieved": round(achieved, 3),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": read_traffic(dom, tag), "algorithmic_flop_per_launch": alg}
     else:
-        alg = KERNELS[dom][3] * B * H * T * hs * 2 + KERNELS[dom][4] * B * H * T * 4
+        alg = KT[dom][3] * B * H * T * hs * 2 + KT[dom][4] * B * H * T * 4
         achieved = alg / (mean_us[dom] * 1e-6) / 1e9
         roof = {"kernel": sym, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -586,8 +630,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": args.dtype,
         "data": "synthetic",
-        "config": {"workload": W["label"],
+        "config": {"workload": W["label"] + (f", attention dropout p={args.dropout}" if drop else ""),
                    "B": B, "H": H, "T": T, "hs": hs, "layers": L, "qkv_scale": W["qkv_scale"],
+                   "dropout": args.dropout,
                    "flop_count": "causal pairs, fwd 4*hs, bwd 8*hs per pair",
                    "parallelism": "single GPU"},
         "value_flashattention_count": round(value_fa, 3),
@@ -601,7 +646,7 @@ def main() -> int:
     if args.cpu_slices > 0:
         print(f"[bench] timing the CPU oracle on {args.cpu_slices} slices", file=sys.stderr,
               flush=True)
-        out["cpu_baseline"] = cpu_baseline(host, scale, args.cpu_slices)
+        out["cpu_baseline"] = cpu_baseline(host, scale, args.cpu_slices, args.dropout)
     print(json.dumps(out), flush=True)
     return 0
 
