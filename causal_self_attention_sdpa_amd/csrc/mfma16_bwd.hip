@@ -49,6 +49,12 @@
 #ifndef GATTN_DQ_OCC
 #define GATTN_DQ_OCC 2
 #endif
+#ifndef GATTN_DKDV_DROP_OCC
+#define GATTN_DKDV_DROP_OCC 2
+#endif
+#ifndef GATTN_DQ_DROP_OCC
+#define GATTN_DQ_DROP_OCC 2
+#endif
 
 namespace gattn {
 namespace {
@@ -154,14 +160,17 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
 
 // The keep bytes of the 8 lanes 8a .. 8a+7 (lane 8a + r passes `byte`, r =
 // lane & 7): byte e of (lo, hi) as one 64-bit word is lane 8a + e's byte.
+// Placement by per-lane shifts and a bit-field insert (no compares).
 __device__ __forceinline__ void gather8(uint32_t byte, int r, uint32_t& lo, uint32_t& hi) {
+  const uint32_t s1 = 8u * (r & 1), s2 = 8u * (r & 2);  // 0 or 8; 0 or 16
+  const uint32_t m4 = 0u - uint32_t((r >> 2) & 1);      // all ones for the upper 4 lanes
   const uint32_t p1 = xor_lane<1>(byte);
-  const uint32_t x16 = (r & 1) ? (p1 | (byte << 8)) : (byte | (p1 << 8));
+  const uint32_t x16 = (byte << s1) | (p1 << (8u - s1));
   const uint32_t p2 = xor_lane<2>(x16);
-  const uint32_t x32 = (r & 2) ? (p2 | (x16 << 16)) : (x16 | (p2 << 16));
+  const uint32_t x32 = (x16 << s2) | (p2 << (16u - s2));
   const uint32_t p4 = xor_lane<4>(x32);
-  lo = (r & 4) ? p4 : x32;
-  hi = (r & 4) ? x32 : p4;
+  lo = (p4 & m4) | (x32 & ~m4);
+  hi = (x32 & m4) | (p4 & ~m4);
 }
 
 // Keep bits of this lane's two runs of 8 queries in query block qb (run t:
@@ -202,9 +211,9 @@ __device__ __forceinline__ void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb
       float p = __builtin_amdgcn_exp2f(fmaf(s[8 * t + e], c, -le));
       if (MASK && krow > qs0 + ql + e) p = 0.f;
       if constexpr (DROP) {
-        const uint32_t wb = w[t][e >> 2];
-        pv[e] = keep_or_zero(p, wb, 8 * (e & 3));
-        dsv[e] = p * (keep_or_zero(dp[8 * t + e] * zs, wb, 8 * (e & 3)) - De);
+        const uint32_t m = keep_mask(w[t][e >> 2], 8 * (e & 3));
+        pv[e] = __uint_as_float(__float_as_uint(p) & m);
+        dsv[e] = p * (__uint_as_float(__float_as_uint(dp[8 * t + e] * zs) & m) - De);
       } else {
         pv[e] = p;
         dsv[e] = p * (dp[8 * t + e] - De);
@@ -266,7 +275,7 @@ __device__ __forceinline__ void dkdv_step_diag(const uint16_t* Qb, const uint16_
 // strides are the compile-time HS (the strides' registers and multiplies
 // would otherwise push this kernel into spills).  DROP: dropout with dr.
 template <class E, int HS, bool STRIDED, bool DROP>
-__global__ __launch_bounds__(kThreads, GATTN_DKDV_OCC) void dkdv16_kernel(
+__global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_OCC) void dkdv16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
     const float* __restrict__ Dg, const float* __restrict__ L2g, uint16_t* __restrict__ dk,
@@ -406,6 +415,15 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
   constexpr int NKB = KIND == kDiagLo ? 1 : 2;  // 32-key blocks computed
   constexpr int KD = KIND == kDiagLo ? 0 : (KIND == kDiagHi ? 1 : -1);  // the diagonal block
   u32x4 dsp[2][2];
+  // Keep bits of the step's runs, drawn before the S / dP MFMAs so that the
+  // generator's vector ALU work overlaps them.
+  uint32_t bits[2][2] = {{0xFFu, 0xFFu}, {0xFFu, 0xFFu}};
+  if constexpr (DROP) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) bits[kb][t] = keep_bits8(qrow, g0 + 4 * kb + 2 * t, bh, dr);
+  }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     f32x16 st = {}, dpt = {};
@@ -416,15 +434,13 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      uint32_t bits = 0xFFu;
-      if constexpr (DROP) bits = keep_bits8(qrow, g0 + 4 * kb + 2 * t, bh, dr);
       float dsv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float p = __builtin_amdgcn_exp2f(fmaf(st[8 * t + e], c, -lse2));
         if (kb == KD && 16 * t + e > dn) p = 0.f;
         if constexpr (DROP)
-          dsv[e] = p * (keep_or_zero(dpt[8 * t + e] * dr.zs, bits, e) - Dq);
+          dsv[e] = p * (keep_or_zero(dpt[8 * t + e] * dr.zs, bits[kb][t], e) - Dq);
         else
           dsv[e] = p * (dpt[8 * t + e] - Dq);
       }
@@ -450,7 +466,7 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
 }
 
 template <class E, int HS, bool STRIDED, bool DROP>  // STRIDED, DROP as for the dK/dV kernel
-__global__ __launch_bounds__(kThreads, GATTN_DQ_OCC) void dq16_kernel(
+__global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) void dq16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, float* __restrict__ Dg,
