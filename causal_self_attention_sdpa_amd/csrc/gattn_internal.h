@@ -57,27 +57,39 @@ __host__ __device__ inline uint32_t slice_span_bytes(const Layout& l, int T, int
 }
 
 // Split of the key range for the forward of the newest Tq tokens (decode):
-// nqb 32-query blocks, nsplit key ranges of tps 64-key tiles each, sized so
-// that about 2048 single-wavefront workgroups cover the GPU.  No split (one
-// workgroup per query block writes the result directly, no merge launch)
-// when a block has at most 4 tiles or there are already 1024 blocks.  The
-// workspace size and the launch both derive from this one function.
+// nqb 32-query blocks; each block's key tiles (64 keys) are divided among
+// nsplit workgroups of tps tiles, and a workgroup's tiles among its nw
+// wavefronts (which merge through LDS).  A block with at most 4 tiles, or
+// 1024 blocks, runs one single-wavefront workgroup per block.  Otherwise nw =
+// GATTN_DEC_NW; when the blocks alone give at least GATTN_DEC_DIRECT_WAVES
+// wavefronts there is no split (one launch, no workspace); else the key range
+// is split so that about 2048 wavefronts stream it, every split keeping at
+// least nw tiles.  The workspace size and the launch both derive from this
+// one function.
+#ifndef GATTN_DEC_NW
+#define GATTN_DEC_NW 4
+#endif
+#ifndef GATTN_DEC_DIRECT_WAVES
+#define GATTN_DEC_DIRECT_WAVES 512
+#endif
 struct DecodeSplit {
-  int nqb, nsplit, tps;
+  int nqb, nsplit, tps, nw;
 };
 inline DecodeSplit decode_split(int BH, int Tq, int Tk) {
   DecodeSplit d;
   d.nqb = (Tq + 31) / 32;
   const int ntiles = (Tk + 63) / 64;
   const long blocks = long(BH) * d.nqb;
-  if (ntiles <= 4 || blocks >= 1024) {
-    d.tps = ntiles;
-    d.nsplit = 1;
-    return d;
-  }
-  int want = int((2048 + blocks - 1) / blocks);
-  want = want < 1 ? 1 : (want > ntiles ? ntiles : want);
-  d.tps = (ntiles + want - 1) / want;
+  d.tps = ntiles;
+  d.nsplit = 1;
+  d.nw = 1;
+  if (ntiles <= 4 || blocks >= 1024) return d;
+  d.nw = GATTN_DEC_NW;
+  if (blocks * d.nw >= GATTN_DEC_DIRECT_WAVES) return d;
+  long want = (2048 + blocks * d.nw - 1) / (blocks * d.nw);
+  const long cap = ntiles / d.nw > 0 ? ntiles / d.nw : 1;
+  want = want > cap ? cap : want;
+  d.tps = int((ntiles + want - 1) / want);
   d.nsplit = (ntiles + d.tps - 1) / d.tps;
   return d;
 }

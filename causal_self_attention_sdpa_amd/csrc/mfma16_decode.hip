@@ -9,13 +9,16 @@
 // that forward.
 //
 // With few queries the work is reading K and V once (HBM-bound), so the key
-// range is split: workgroup (b, h, 32-query block, split s) is one wavefront
-// that streams key tiles [s*tps, ...) of 64 keys through double-buffered
-// swizzled LDS tiles (LDS DMA), runs the forward's tile step (S^T = K Q^T on
-// MFMA, base-2 online softmax, O^T += V^T P^T) and writes its normalised
-// partial output and log-sum-exp in float32.  dec16_combine merges the
-// splits: lse = log sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s, rounded
-// once to the 16-bit type.  Rows (or whole splits) that see no key keep
+// range is split twice.  Workgroup (b, h, 32-query block, split s) owns key
+// tiles [s*tps, ...) of 64 keys; each of its NW wavefronts streams every
+// NW-th of those tiles through its own double-buffered swizzled LDS tiles
+// (LDS DMA) and runs the forward's tile step (S^T = K Q^T on MFMA, base-2
+// online softmax, O^T += V^T P^T).  The wavefronts then merge their (max,
+// sum, output) states through LDS.  With one split the workgroup writes o
+// and lse; otherwise it writes its normalised partial output and
+// log-sum-exp in float32 and dec16_combine merges the splits:
+// lse = log sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s, rounded once
+// to the 16-bit type.  Rows (or whole splits) that see no key keep
 // m = -inf and l = 0 and contribute exp(-inf) = 0; every step is written so
 // that no NaN arises from -inf - (-inf).
 #include <cmath>
@@ -102,8 +105,8 @@ __device__ __forceinline__ void dec_tile(const uint16_t* Kb, const uint16_t* Vb,
 // scores, -inf when the row saw none of its keys).
 // DIRECT (one split): the workgroup's result is the final one; it writes o
 // (16-bit, layout lo) and lse instead of partials.
-template <class E, int HS, bool STRIDED, bool DIRECT>
-__global__ __launch_bounds__(64) void dec16_kernel(const uint16_t* __restrict__ q,
+template <class E, int HS, bool STRIDED, bool DIRECT, int NW>
+__global__ __launch_bounds__(64 * NW) void dec16_kernel(const uint16_t* __restrict__ q,
                                                    const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v,
                                                    float* __restrict__ opart,
@@ -113,10 +116,12 @@ __global__ __launch_bounds__(64) void dec16_kernel(const uint16_t* __restrict__ 
                                                    int Tk, int nqb, int nsplit, int tps,
                                                    float scale, Layout lq, Layout lk, Layout lo) {
   constexpr int KSTEP = HS / 16, DB = HS / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * HS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][kBN * HS];
+  // Per wavefront: a K ring and a V ring of two tiles; after the loop the same
+  // memory holds the wavefronts' states for the merge.
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NW][2][kBN * HS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NW][2][kBN * HS];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int sp = int(blockIdx.x) % nsplit;
   const int qb = (int(blockIdx.x) / nsplit) % nqb;
@@ -126,7 +131,9 @@ __global__ __launch_bounds__(64) void dec16_kernel(const uint16_t* __restrict__ 
   const int last = off + row;  // newest key this lane's query sees
   // Key tiles any query of the block sees, and this split's share of them.
   const int kmax = off + min(qb * 32 + 31, Tq - 1);
-  const int t0 = sp * tps, t1 = min(kmax / kBN + 1, t0 + tps);
+  // This wavefront's tiles: t0 + w, t0 + w + NW, ... below t1.
+  const int t0 = sp * tps + w, t1 = min(kmax / kBN + 1, sp * tps + tps);
+  const int ntw = t0 < t1 ? (t1 - t0 + NW - 1) / NW : 0;
 
   const int rq = STRIDED ? int(lq.st) : HS, rk = STRIDED ? int(lk.st) : HS;
   const rsrc_t wq = make_rsrc(q + slice_offset(lq, bh, H), slice_span_bytes(lq, Tq, HS, 2));
@@ -140,34 +147,97 @@ __global__ __launch_bounds__(64) void dec16_kernel(const uint16_t* __restrict__ 
   st.m = -INFINITY;
   st.l = 0.f;
 
-  if (t0 < t1) {
+  if (ntw > 0) {
     const float c = scale * kLog2e;
     const LaneOffsets<HS> L(lane);
-    dma_tile<HS, kBN, 1>(wk, t0 * kBN, rk, Ks[0], 0, lane);
-    dma_tile<HS, kBN, 1>(wv, t0 * kBN, rk, Vs[0], 0, lane);
+    dma_tile<HS, kBN, 1>(wk, t0 * kBN, rk, Ks[w][0], 0, lane);
+    dma_tile<HS, kBN, 1>(wv, t0 * kBN, rk, Vs[w][0], 0, lane);
     // Q^T as the MFMA B operand (rows past Tq read as zero).
     u32x4 qf[KSTEP];
 #pragma unroll
     for (int ks = 0; ks < KSTEP; ++ks)
       qf[ks] = bload16(wq, uint32_t(row * rq + 16 * ks + 8 * h) * 2);
+    // The rings are private to the wavefront: waiting for its own LDS DMA
+    // is enough (no workgroup barrier inside the loop).
     wait_vmem();
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     auto step = [&](int i, auto bufc) {
       constexpr int buf = decltype(bufc)::value;
-      const int t = t0 + i;
-      if (t + 1 < t1) {
-        dma_tile<HS, kBN, 1>(wk, (t + 1) * kBN, rk, Ks[buf ^ 1], 0, lane);
-        dma_tile<HS, kBN, 1>(wv, (t + 1) * kBN, rk, Vs[buf ^ 1], 0, lane);
+      const int t = t0 + i * NW;
+      if (i + 1 < ntw) {
+        dma_tile<HS, kBN, 1>(wk, (t + NW) * kBN, rk, Ks[w][buf ^ 1], 0, lane);
+        dma_tile<HS, kBN, 1>(wv, (t + NW) * kBN, rk, Vs[w][buf ^ 1], 0, lane);
       }
       const int key0 = t * kBN;
       if (key0 + kBN - 1 > off + qb * 32)  // some key may lie past some query
-        dec_tile<E, HS, true>(Ks[buf], Vs[buf], key0, last, h, c, L, qf, st);
+        dec_tile<E, HS, true>(Ks[w][buf], Vs[w][buf], key0, last, h, c, L, qf, st);
       else
-        dec_tile<E, HS, false>(Ks[buf], Vs[buf], key0, last, h, c, L, qf, st);
+        dec_tile<E, HS, false>(Ks[w][buf], Vs[w][buf], key0, last, h, c, L, qf, st);
       wait_vmem();
-      __syncthreads();
+      __builtin_amdgcn_wave_barrier();
     };
-    ring_loop<2>(t1 - t0, step);
+    ring_loop<2>(ntw, step);
+  }
+  if constexpr (NW > 1) {
+    // Merge the wavefronts' states: each writes its max (m, raw score units;
+    // -inf if it saw none of the row's keys), sum l and unnormalised output
+    // rows to LDS, then every thread combines a pair of output elements.
+    constexpr int RS = HS + 4;  // padded row of the output state (floats)
+    float* const mst = reinterpret_cast<float*>(&Ks[0][0][0]);       // [NW][32]
+    float* const lst = mst + NW * 32;                                 // [NW][32]
+    float* const ost = lst + NW * 32;                                 // [NW][32][RS]
+    static_assert(sizeof(float) * NW * 32 * (RS + 2) <= sizeof(Ks), "merge state fits");
+    const float lw = halves_sum(st.l);
+    __syncthreads();  // every wavefront is done with its tiles
+    if (h == 0) {
+      mst[w * 32 + n] = st.m;
+      lst[w * 32 + n] = lw;
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(ost + (w * 32 + n) * RS + db * 32 + 8 * g + 4 * h) =
+            f32x4{st.oacc[db][4 * g], st.oacc[db][4 * g + 1], st.oacc[db][4 * g + 2],
+                  st.oacc[db][4 * g + 3]};
+    __syncthreads();
+    const float c = scale * kLog2e;
+    for (int idx = threadIdx.x; idx < 32 * HS / 2; idx += 64 * NW) {
+      const int r = idx / (HS / 2), d = 2 * (idx % (HS / 2));
+      float M = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < NW; ++u) M = fmaxf(M, mst[u * 32 + r]);
+      float Ls = 0.f, a0 = 0.f, a1 = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < NW; ++u) {
+          const float wt = __builtin_amdgcn_exp2f((mst[u * 32 + r] - M) * c);  // -inf -> 0
+          Ls += wt * lst[u * 32 + r];
+          a0 = fmaf(wt, ost[(u * 32 + r) * RS + d], a0);
+          a1 = fmaf(wt, ost[(u * 32 + r) * RS + d + 1], a1);
+        }
+      }
+      const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+      const int rr = qb * 32 + r;
+      if constexpr (DIRECT) {  // split 0 holds key 0, seen by every query: Ls > 0
+        const rsrc_t wo = make_rsrc(o + slice_offset(lo, bh, H), slice_span_bytes(lo, Tq, HS, 2));
+        const int ro = STRIDED ? int(lo.st) : HS;
+        __builtin_amdgcn_raw_buffer_store_b32(E::pack(a0 * inv, a1 * inv), wo,
+                                              uint32_t(rr * ro + d) * 2, 0, 0);
+        if (lse != nullptr && d == 0)
+          bstoref(make_rsrc(lse + long(bh) * Tq, uint32_t(Tq) * 4), uint32_t(rr) * 4,
+                  M * scale + logf(Ls));
+      } else {
+        const long pbase = (long(bh) * nsplit + sp) * Tq;
+        const rsrc_t wp = make_rsrc(opart + pbase * HS, uint32_t(Tq) * HS * 4);
+        bstore8(wp, uint32_t(rr * HS + d) * 4,
+                u32x2{__float_as_uint(a0 * inv), __float_as_uint(a1 * inv)});
+        if (d == 0)
+          bstoref(make_rsrc(lpart + pbase, uint32_t(Tq) * 4), uint32_t(rr) * 4,
+                  Ls > 0.f ? M * scale + logf(Ls) : -INFINITY);
+      }
+    }
+    return;
   }
 
   // O^T register i of lane (n, h): column d = db*32 + 8*(i/4) + 4h + i%4 of
@@ -265,11 +335,17 @@ hipError_t dec16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          is_contiguous(lo, H, Tq, HS));
   const dim3 grid(unsigned(BH * ds.nqb * ds.nsplit));
   const bool direct = ds.nsplit == 1;
-  auto kern = strided ? (direct ? dec16_kernel<E, HS, true, true> : dec16_kernel<E, HS, true, false>)
-                      : (direct ? dec16_kernel<E, HS, false, true>
-                                : dec16_kernel<E, HS, false, false>);
-  hipError_t e = launch(kern, grid, dim3(64), s, q, k, v, opart, lpart, o, lse, H, Tq, Tk, ds.nqb,
-                        ds.nsplit, ds.tps, scale, lq, lk, lo);
+  auto pick = [&](auto nwc) {
+    constexpr int NW = decltype(nwc)::value;
+    return strided ? (direct ? dec16_kernel<E, HS, true, true, NW>
+                             : dec16_kernel<E, HS, true, false, NW>)
+                   : (direct ? dec16_kernel<E, HS, false, true, NW>
+                             : dec16_kernel<E, HS, false, false, NW>);
+  };
+  auto kern = ds.nw == 4 ? pick(std::integral_constant<int, 4>{})
+                         : pick(std::integral_constant<int, 1>{});
+  hipError_t e = launch(kern, grid, dim3(64 * ds.nw), s, q, k, v, opart, lpart, o, lse, H, Tq, Tk,
+                        ds.nqb, ds.nsplit, ds.tps, scale, lq, lk, lo);
   if (e != hipSuccess || direct) return e;
   const long rows = long(BH) * Tq;
   return launch(dec16_combine<E, HS>, dim3(unsigned((rows + 3) / 4)), dim3(256), s, opart, lpart,
