@@ -379,8 +379,8 @@ def main() -> int:
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the attention core shards over (b, h) with no exchange; see the design notes).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the "
+              "attention core shards over (b, h) with no exchange between GPUs).",
               file=sys.stderr)
         return 2
 
