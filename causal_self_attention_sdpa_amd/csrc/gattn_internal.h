@@ -59,8 +59,8 @@ __host__ __device__ inline uint32_t slice_span_bytes(const Layout& l, int T, int
 // Split of the key range for the forward of the newest Tq tokens (decode):
 // nqb 32-query blocks; each block's key tiles (64 keys) are divided among
 // nsplit workgroups of tps tiles, and a workgroup's tiles among its nw
-// wavefronts (which merge through LDS).  A block with at most 4 tiles, or
-// 1024 blocks, runs one single-wavefront workgroup per block.  Otherwise nw =
+// wavefronts (which merge through LDS).  A block with one tile, or 1024
+// blocks, runs one single-wavefront workgroup per block.  Otherwise nw =
 // GATTN_DEC_NW; when the blocks alone give at least GATTN_DEC_DIRECT_WAVES
 // wavefronts there is no split (one launch, no workspace); else the key range
 // is split so that about 2048 wavefronts stream it, every split keeping at
@@ -83,7 +83,7 @@ inline DecodeSplit decode_split(int BH, int Tq, int Tk) {
   d.tps = ntiles;
   d.nsplit = 1;
   d.nw = 1;
-  if (ntiles <= 4 || blocks >= 1024) return d;
+  if (ntiles < 2 || blocks >= 1024) return d;
   d.nw = GATTN_DEC_NW;
   if (blocks * d.nw >= GATTN_DEC_DIRECT_WAVES) return d;
   long want = (2048 + blocks * d.nw - 1) / (blocks * d.nw);
