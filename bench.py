@@ -358,6 +358,10 @@ def main() -> int:
                          "layer against --kv-len kept keys; generate: the pages' generate loop")
     ap.add_argument("--kv-len", type=int, default=1024)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="gpt2-124m")
+    ap.add_argument("--seq-len", type=int, default=0,
+                    help="override the workload's T (train mode; a scaling probe, not a workload "
+                         "of the pages)")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's B (train mode)")
     ap.add_argument("--dtype", choices=("bf16", "f16"), default="bf16",
                     help="16-bit storage type of q, k, v, o and the gradients")
     ap.add_argument("--layout", choices=("contiguous", "fused", "copies"), default="contiguous",
@@ -407,7 +411,11 @@ def main() -> int:
 
     tdt = torch.bfloat16 if args.dtype == "bf16" else torch.float16
     dcode = ga.BF16 if args.dtype == "bf16" else ga.F16
-    W = WORKLOADS[args.workload]
+    W = dict(WORKLOADS[args.workload])
+    if args.seq_len or args.batch:
+        W["T"] = args.seq_len or W["T"]
+        W["B"] = args.batch or W["B"]
+        W["label"] += f" (B, T overridden to {W['B']}, {W['T']})"
     B, H, T, hs, L = W["B"], W["H"], W["T"], W["hs"], W["layers"]
     tag = f"b{B}h{H}t{T}"
     metric = f"causal attention fwd+bwd TFLOP/s at B{B} H{H} T{T} hs{hs}; % of bf16 MFMA peak"
