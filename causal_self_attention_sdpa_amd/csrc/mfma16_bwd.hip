@@ -242,13 +242,25 @@ __device__ __forceinline__ void dkdv_step_full(const uint16_t* Qb, const uint16_
                                       const LaneOffsets<HS>& L, DkdvRegs<HS>& R, uint32_t bh,
                                       const Dropout& dr) {
   using C = DkdvCfg<HS>;
+  if constexpr (DROP) {  // block by block: the generator's registers leave no room for both
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    uint32_t w[2][2] = {};
-    if constexpr (DROP) dkdv_keep(qs0, qb, krow, h, bh, dr, w);
-    f32x16 s, dp;
-    dkdv_sdp<E, HS>(Qb, Gb, qb, L, R, s, dp);
-    dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R, w, dr.zs);
+    for (int qb = 0; qb < C::QB; ++qb) {
+      uint32_t w[2][2] = {};
+      dkdv_keep(qs0, qb, krow, h, bh, dr, w);
+      f32x16 s, dp;
+      dkdv_sdp<E, HS>(Qb, Gb, qb, L, R, s, dp);
+      dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R, w, dr.zs);
+    }
+  } else {
+    // S and dP of both blocks first: block 1's MFMAs run while block 0's
+    // weights and dS are computed on the vector ALU.
+    static_assert(C::QB == 2, "two query blocks per step");
+    const uint32_t w[2][2] = {};
+    f32x16 s0, dp0, s1, dp1;
+    dkdv_sdp<E, HS>(Qb, Gb, 0, L, R, s0, dp0);
+    dkdv_sdp<E, HS>(Qb, Gb, 1, L, R, s1, dp1);
+    dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, 0, qs0, krow, h, c, L, s0, dp0, R, w, dr.zs);
+    dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, 1, qs0, krow, h, c, L, s1, dp1, R, w, dr.zs);
   }
 }
 
