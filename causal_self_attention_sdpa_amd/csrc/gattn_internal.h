@@ -72,11 +72,37 @@ __host__ __device__ inline uint32_t slice_span_bytes(const Layout& l, int T, int
 #ifndef GATTN_DEC_DIRECT_WAVES
 #define GATTN_DEC_DIRECT_WAVES 512
 #endif
+//
+// One new token (Tq = 1) takes the vector-ALU path instead: workgroups of
+// GATTN_DEC1_NW wavefronts, each streaming a contiguous run of the
+// workgroup's kps keys; no split when the heads give 1024 wavefronts, else
+// about 2048 wavefronts with at least 64 keys each.
+#ifndef GATTN_DEC1_NW
+#define GATTN_DEC1_NW 8
+#endif
 struct DecodeSplit {
   int nqb, nsplit, tps, nw;
+  int kps;  // one-token path: keys per split (0 on the MFMA path)
 };
 inline DecodeSplit decode_split(int BH, int Tq, int Tk) {
   DecodeSplit d;
+  d.kps = 0;
+  if (Tq == 1) {
+    d.nqb = 1;
+    d.tps = 0;
+    d.nw = GATTN_DEC1_NW;
+    const long waves = long(BH) * d.nw;
+    long ns = 1;
+    if (waves < 1024) {
+      ns = (2048 + waves - 1) / waves;
+      const long cap = (Tk + 64L * d.nw - 1) / (64L * d.nw);  // >= 64 keys per wavefront
+      ns = ns > cap ? cap : ns;
+      ns = ns < 1 ? 1 : ns;
+    }
+    d.kps = int((Tk + ns - 1) / ns);
+    d.nsplit = (Tk + d.kps - 1) / d.kps;
+    return d;
+  }
   d.nqb = (Tq + 31) / 32;
   const int ntiles = (Tk + 63) / 64;
   const long blocks = long(BH) * d.nqb;

@@ -73,6 +73,7 @@ struct F16 {
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // ds_read_b64_tr_b16 (gfx950 LDS transpose read).  Within each group of 16
 // lanes, every lane names an 8-byte segment (4 bf16); output element e of

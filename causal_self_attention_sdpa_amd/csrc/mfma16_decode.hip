@@ -280,6 +280,158 @@ __global__ __launch_bounds__(64 * NW) void dec16_kernel(const uint16_t* __restri
             lt > 0.f ? st.m * scale + logf(lt) : -INFINITY);
 }
 
+// One new token (Tq = 1): the query is the newest position, so it sees every
+// kept key (no mask), and an MFMA tile would leave 31 of its 32 query rows
+// idle.  Vector arithmetic streams K and V instead.  Workgroup (b, h, split)
+// has NW wavefronts, each taking a contiguous run of the split's keys.  A key
+// row is read by LPK = HS/8 lanes (16 bytes each), so one load instruction
+// covers KPI = 64/LPK consecutive keys; the lanes of a key add their partial
+// dot products (xor shuffles) and each group of LPK lanes keeps its own
+// online softmax state (max m in base-2 score units, sum l) and its 8 output
+// columns, for the keys g, g + KPI, ... of the run.  U iterations of loads
+// are in flight together.  The groups merge by xor shuffles, the wavefronts
+// through LDS; the result is o and lse (DIRECT) or the split's normalised
+// partial output and log-sum-exp, merged by dec16_combine.
+template <class E, int HS, bool STRIDED, bool DIRECT, int NW>
+__global__ __launch_bounds__(64 * NW) void dec1_kernel(const uint16_t* __restrict__ q,
+                                                       const uint16_t* __restrict__ k,
+                                                       const uint16_t* __restrict__ v,
+                                                       float* __restrict__ opart,
+                                                       float* __restrict__ lpart,
+                                                       uint16_t* __restrict__ o,
+                                                       float* __restrict__ lse, int H, int Tk,
+                                                       int nsplit, int kps, float scale,
+                                                       Layout lq, Layout lk, Layout lo) {
+  constexpr int LPK = HS / 8, KPI = 64 / LPK, U = 4;
+  __shared__ float sm[NW], sl[NW];
+  __shared__ __attribute__((aligned(16))) float so[NW][HS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane / LPK, cc = lane % LPK;
+  const int sp = int(blockIdx.x) % nsplit, bh = int(blockIdx.x) / nsplit;
+  const int k0 = sp * kps, k1 = min(Tk, k0 + kps);
+  const int per = ((k1 - k0 + NW - 1) / NW + KPI - 1) / KPI * KPI;  // keys per wavefront
+  const int a = k0 + w * per, b = min(k1, a + per);
+  const int rk = STRIDED ? int(lk.st) : HS;
+  const int64_t kbase = slice_offset(lk, bh, H);
+  const uint32_t kbytes = slice_span_bytes(lk, Tk, HS, 2);
+  const rsrc_t wk = make_rsrc(k + kbase, kbytes), wv = make_rsrc(v + kbase, kbytes);
+  const float c = scale * kLog2e;
+  // This lane's 8 query elements, scaled into base-2 score units.
+  const u32x4 qr = bload16(make_rsrc(q + slice_offset(lq, bh, H), HS * 2), uint32_t(cc * 16));
+  float qf[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    qf[2 * e] = E::lo(qr[e]) * c;
+    qf[2 * e + 1] = E::hi(qr[e]) * c;
+  }
+  float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  // Batches of U iterations; the next batch's loads are issued before the
+  // current one is computed (rows past the slice read as zero and are masked).
+  auto load = [&](int base, u32x4 (&kr)[U], u32x4 (&vr)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t off = uint32_t((base + u * KPI + g) * rk + cc * 8) * 2;
+      kr[u] = bload16(wk, off);
+      vr[u] = bload16(wv, off);
+    }
+  };
+  auto consume = [&](int base, const u32x4 (&kr)[U], const u32x4 (&vr)[U]) {
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t = fmaf(qf[2 * e], E::lo(kr[u][e]), t);
+        t = fmaf(qf[2 * e + 1], E::hi(kr[u][e]), t);
+      }
+#pragma unroll
+      for (int off = LPK / 2; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+      s[u] = base + u * KPI + g < b ? t : -INFINITY;
+    }
+    float mb = s[0];
+#pragma unroll
+    for (int u = 1; u < U; ++u) mb = fmaxf(mb, s[u]);
+    if (mb > m) {  // m = -inf at first: alpha = 0
+      const float al = __builtin_amdgcn_exp2f(m - mb);
+      l *= al;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= al;
+      m = mb;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = s[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[u] - m);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(p, E::lo(vr[u][e]), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(p, E::hi(vr[u][e]), acc[2 * e + 1]);
+      }
+    }
+  };
+  constexpr int STEP = KPI * U;
+  u32x4 ka[U], va[U], kb[U], vb[U];
+  if (a < b) load(a, ka, va);
+  for (int base = a; base < b; base += 2 * STEP) {
+    if (base + STEP < b) load(base + STEP, kb, vb);
+    consume(base, ka, va);
+    if (base + STEP >= b) break;
+    if (base + 2 * STEP < b) load(base + 2 * STEP, ka, va);
+    consume(base + STEP, kb, vb);
+  }
+  // Merge the lane groups (a group that saw no key has m = -inf, l = 0).
+#pragma unroll
+  for (int off = LPK; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off, 64), l2 = __shfl_xor(l, off, 64);
+    const float M = fmaxf(m, m2);
+    const float a1 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+    const float a2 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+    l = l * a1 + l2 * a2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * a1 + __shfl_xor(acc[e], off, 64) * a2;
+    m = M;
+  }
+  if (lane == 0) {
+    sm[w] = m;
+    sl[w] = l;
+  }
+  if (g == 0) {
+    *reinterpret_cast<f32x4*>(&so[w][cc * 8]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(&so[w][cc * 8 + 4]) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+  __syncthreads();
+  // Merge the wavefronts: thread t < HS/2 finishes columns 2t, 2t+1.  The
+  // split holds at least one key, so M is finite and L > 0.
+  if (int(threadIdx.x) < HS / 2) {
+    const int d = 2 * int(threadIdx.x);
+    float M = sm[0];
+#pragma unroll
+    for (int u = 1; u < NW; ++u) M = fmaxf(M, sm[u]);
+    float L = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < NW; ++u) {
+      const float wt = __builtin_amdgcn_exp2f(sm[u] - M);  // -inf -> 0
+      L = fmaf(wt, sl[u], L);
+      o0 = fmaf(wt, so[u][d], o0);
+      o1 = fmaf(wt, so[u][d + 1], o1);
+    }
+    const float inv = 1.f / L;
+    const float ls = (M + log2f(L)) * kLn2;  // natural log-sum-exp
+    if constexpr (DIRECT) {
+      uint16_t* orow = o + slice_offset(lo, bh, H);
+      *reinterpret_cast<uint32_t*>(orow + d) = E::pack(o0 * inv, o1 * inv);
+      if (lse != nullptr && d == 0) lse[bh] = ls;
+    } else {
+      float* op = opart + (long(bh) * nsplit + sp) * HS;
+      *reinterpret_cast<float2*>(op + d) = float2{o0 * inv, o1 * inv};
+      if (d == 0) lpart[long(bh) * nsplit + sp] = ls;
+    }
+  }
+}
+
 // One wavefront per (b, h, query): merge the splits, store o (16-bit, round
 // to nearest even) and lse.  Lane j holds elements 2j, 2j+1 of the row.
 template <class E, int HS>
@@ -335,6 +487,17 @@ hipError_t dec16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          is_contiguous(lo, H, Tq, HS));
   const dim3 grid(unsigned(BH * ds.nqb * ds.nsplit));
   const bool direct = ds.nsplit == 1;
+  if (ds.kps > 0) {  // one new token: the vector-ALU kernel
+    constexpr int NW = GATTN_DEC1_NW;
+    auto k1 = strided ? (direct ? dec1_kernel<E, HS, true, true, NW> : dec1_kernel<E, HS, true, false, NW>)
+                      : (direct ? dec1_kernel<E, HS, false, true, NW>
+                                : dec1_kernel<E, HS, false, false, NW>);
+    hipError_t e = launch(k1, grid, dim3(64 * NW), s, q, k, v, opart, lpart, o, lse, H, Tk,
+                          ds.nsplit, ds.kps, scale, lq, lk, lo);
+    if (e != hipSuccess || direct) return e;
+    return launch(dec16_combine<E, HS>, dim3(unsigned((BH + 3) / 4)), dim3(256), s, opart, lpart,
+                  o, lse, BH, H, Tq, ds.nsplit, lo);
+  }
   auto pick = [&](auto nwc) {
     constexpr int NW = decltype(nwc)::value;
     return strided ? (direct ? dec16_kernel<E, HS, true, true, NW>
