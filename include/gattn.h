@@ -125,12 +125,13 @@ int gattn_fwd_strided(const void* q, const void* k, const void* v, void* o, floa
  *   workspace: at least gattn_fwd_decode_workspace_bytes() bytes, 256-byte
  *             aligned, overwritten (partial results of the key splits); may be
  *             NULL when that size is 0 (float32, or a single split).
- * The 16-bit path splits the key range over workgroups (each streams its keys
- * from HBM once) and merges the partial results in a second kernel, unless
- * one split per 32-query block suffices (at most 4 key tiles of 64, or 1024
- * blocks already); float32 runs one wavefront per query.  INVALID_ARG also
- * for Tq < 1 or Tk < Tq; WORKSPACE for a missing, misaligned or short
- * workspace when one is needed.
+ * The 16-bit path reads every kept key and value from HBM once, split over
+ * the wavefronts of a workgroup (merged through LDS) and, when the heads
+ * alone would leave the GPU idle, over several workgroups whose partial
+ * results a second kernel merges (that case needs the workspace).  Tq = 1
+ * runs a vector-ALU kernel, Tq > 1 the MFMA kernel; float32 runs one
+ * wavefront per query.  INVALID_ARG also for Tq < 1 or Tk < Tq; WORKSPACE for
+ * a missing, misaligned or short workspace when one is needed.
  */
 int gattn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int Tq, int Tk, int hs, float scale, int dtype,
