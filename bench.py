@@ -112,8 +112,25 @@ def measured_peaks(torch, dev):
         y.copy_(x)
     torch.cuda.synchronize()
     copy = 2.0 * x.numel() * 4 * reps / (time.perf_counter() - t0) / 1e9
+    del x, y
+    # a loop of independent bf16 MFMAs on register operands (the library's probe)
+    import causal_self_attention_sdpa_amd as ga
+    lib = ga.load_library()
+    blocks, iters = 2048, 128
+    sink = torch.empty(4 * blocks, dtype=torch.float32, device=dev)
+    sp = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        assert lib.gattn_probe_mfma_bf16(sink.data_ptr(), blocks, iters, sp) == 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        lib.gattn_probe_mfma_bf16(sink.data_ptr(), blocks, iters, sp)
+    torch.cuda.synchronize()
+    mfma = blocks * 4 * iters * 8 * 32768 * 5 / (time.perf_counter() - t0) / 1e12
     return {"bf16_gemm_tflops": round(gemm, 1), "copy_gbs": round(copy, 1),
-            "gemm": "torch.matmul bf16 8192x8192x8192", "copy": "1 GiB device-to-device"}
+            "mfma_loop_bf16_tflops": round(mfma, 1),
+            "gemm": "torch.matmul bf16 8192x8192x8192", "copy": "1 GiB device-to-device",
+            "mfma_loop": "gattn_probe_mfma_bf16: 2048 x 4 wavefronts x 128 x 8 MFMA 32x32x16"}
 
 
 def source_digest(path: str) -> str:
@@ -167,8 +184,20 @@ def cpu_baseline(host_layers, scale, nslices: int, dropout: float = 0.0):
     dt = time.perf_counter() - t0
     ff, fb = flops(len(idx), 1, T, hs)
     nl = idx[-1][0] + 1
+    single = None
+    if dropout == 0.0:
+        # one thread on a tenth of the sample
+        n1 = max(1, len(idx) // 10)
+        t1 = time.perf_counter()
+        oracle.attention_backward(sel["q"][:n1], sel["k"][:n1], sel["v"][:n1], sel["do"][:n1],
+                                  scale, nthreads=1)
+        d1 = time.perf_counter() - t1
+        f1f, f1b = flops(n1, 1, T, hs)
+        single = {"value": round((f1f + f1b) / d1 / 1e12, 6), "cores": 1, "seconds": round(d1, 3),
+                  "sample": f"the first {n1} of those slices"}
     return {"value": round((ff + fb) / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "seconds": round(dt, 3), "single_thread": single,
+            "hardware_concurrency": oracle.hardware_threads(),
             "sample": f"{len(idx)} of the {B * H * len(host_layers)} (layer,b,h) slices "
                       f"(layers 0..{nl - 1}; T={T}, hs={hs}), forward+backward in float64"
                       f"{f' with dropout p={dropout}' if dropout > 0 else ''}, "

@@ -65,6 +65,8 @@ def load_library():
     lib.gattn_bwd_dropout.restype = i
     lib.gattn_dropout_mask.argtypes = [vp, i, i, i, f, u64, u32, vp]
     lib.gattn_dropout_mask.restype = i
+    lib.gattn_probe_mfma_bf16.argtypes = [vp, i, i, vp]
+    lib.gattn_probe_mfma_bf16.restype = i
     lib.gattn_status_string.argtypes = [i]
     lib.gattn_status_string.restype = ctypes.c_char_p
     _lib = lib

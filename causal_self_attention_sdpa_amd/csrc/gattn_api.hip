@@ -218,6 +218,11 @@ int gattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, floa
   return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, li, lo, dr, stream);
 }
 
+int gattn_probe_mfma_bf16(float* sink, int blocks, int iters, hipStream_t stream) {
+  if (sink == nullptr || blocks < 1 || iters < 1) return GATTN_ERR_INVALID_ARG;
+  return status_of(gattn::mfma_loop(sink, blocks, iters, stream));
+}
+
 int gattn_dropout_mask(uint8_t* keep, int B, int H, int T, float p, uint64_t seed,
                        uint32_t offset, hipStream_t stream) {
   if (keep == nullptr || B < 1 || H < 1 || T < 1) return GATTN_ERR_INVALID_ARG;

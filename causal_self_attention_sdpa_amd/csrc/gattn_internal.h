@@ -165,6 +165,9 @@ hipError_t h16_fwd_decode(const uint16_t* q, const uint16_t* k, const uint16_t* 
                           float* lse, int BH, int H, int Tq, int Tk, int hs, float scale,
                           Layout lq, Layout lk, Layout lo, float* opart, float* lpart,
                           const DecodeSplit& ds, bool f16, hipStream_t s);
+// Diagnostic loop of bf16 MFMAs: blocks workgroups of 4 wavefronts, each
+// wavefront iters x 8 MFMAs of 32x32x16; one float per wavefront into sink.
+hipError_t mfma_loop(float* sink, int blocks, int iters, hipStream_t s);
 // Keep decisions (bytes, 1 = kept) of every (b*H + h, i, j), j and i < T.
 hipError_t dropout_mask(uint8_t* keep, int BH, int T, const Dropout& dr, hipStream_t s);
 hipError_t h16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,

@@ -262,6 +262,16 @@ int gattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o
 int gattn_dropout_mask(uint8_t* keep, int B, int H, int T, float p, uint64_t seed,
                        uint32_t offset, hipStream_t stream);
 
+/*
+ * Diagnostic, not part of attention: `blocks` workgroups of 4 wavefronts each
+ * run `iters` rounds of 8 independent bf16 MFMAs (32x32x16, 32768 FLOP each)
+ * on register operands, with no memory traffic, and write one float per
+ * wavefront to sink (device buffer of 4*blocks floats).  Timing it gives the
+ * achievable bf16 MFMA rate at the current clock: FLOP = blocks * 4 * iters *
+ * 8 * 32768.  INVALID_ARG for sink NULL, blocks < 1 or iters < 1.
+ */
+int gattn_probe_mfma_bf16(float* sink, int blocks, int iters, hipStream_t stream);
+
 /* Static, human-readable name of a gattn_status value. */
 const char* gattn_status_string(int status);
 

@@ -243,3 +243,9 @@ def test_dropout_validation(lib):
     assert mask(keep=None) == INVALID
     assert mask(T=0) == INVALID
     assert mask(B=1 << 10, H=1 << 10, T=1 << 10) == INVALID     # 2^40 bytes
+
+
+def test_probe_validation(lib):
+    assert lib.gattn_probe_mfma_bf16(None, 4, 4, None) == INVALID
+    assert lib.gattn_probe_mfma_bf16(P, 0, 4, None) == INVALID
+    assert lib.gattn_probe_mfma_bf16(P, 4, 0, None) == INVALID
