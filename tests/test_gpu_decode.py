@@ -105,13 +105,17 @@ def test_decode_f32(Tq, Tk, hs):
     _check("f32", 2, 3, Tq, Tk, hs)
 
 
-def test_decode_from_a_cache_view():
+@pytest.mark.parametrize("Tq,Tk", [(4, 150), (1, 150), (1, 1000), (4, 1000)])
+def test_decode_from_a_cache_view(Tq, Tk):
     """k, v as the first Tk rows of a (B, H, Tmax, hs) cache whose other rows
     hold NaN, q read from (B, Tq, H, hs) and o written into (B, Tq, H, hs + 8)
-    with NaN poison: same values as the contiguous call, padding untouched."""
+    with NaN poison: same values as the contiguous call, padding untouched.
+    Tq = 1 runs the one-token kernel, Tq = 4 the MFMA kernel; Tk = 1000 splits
+    the key range (a merge launch and the workspace)."""
     import torch
     import causal_self_attention_sdpa_amd as ga
-    B, H, Tq, Tk, Tmax, hs = 2, 3, 4, 150, 256, 64
+    B, H, Tmax, hs = 2, 3, 1024, 64
+    print(f"case decode cache view Tq={Tq} Tk={Tk}", flush=True)
     q, k, v = _kv_inputs(B, H, Tq, Tk, hs, "bf16", 92)
     s = default_scale(hs)
     dt = torch.bfloat16
