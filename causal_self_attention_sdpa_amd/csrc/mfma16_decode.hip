@@ -1,5 +1,7 @@
 // 16-bit (bf16 or fp16) forward of the newest Tq tokens against Tk >= Tq keys
-// on gfx950 MFMA: decoding with the keys and values of earlier tokens kept.
+// on gfx950: decoding with the keys and values of earlier tokens kept.  Tq > 1
+// runs the MFMA kernel (dec16_kernel), one new token the vector-ALU kernel
+// (dec1_kernel, below); both read every kept key and value once.
 //
 // Query i is the token at position Tk - Tq + i of the key sequence and sees
 // keys j <= Tk - Tq + i: the causal mask of "Let's build GPT" (tril, 48:54;
