@@ -249,3 +249,16 @@ def test_probe_validation(lib):
     assert lib.gattn_probe_mfma_bf16(None, 4, 4, None) == INVALID
     assert lib.gattn_probe_mfma_bf16(P, 0, 4, None) == INVALID
     assert lib.gattn_probe_mfma_bf16(P, 4, 0, None) == INVALID
+
+
+def test_header_is_plain_c_and_the_c_caller_links(tmp_path):
+    """include/gattn.h compiles as C11 with warnings as errors, and the plain-C
+    caller of the GPU tests (tests/c_abi) links against libgattn.so, the
+    oracle library and the HIP runtime (built here into a scratch path)."""
+    import importlib.util
+    path = os.path.join(ROOT, "tests", "c_abi", "build.py")
+    spec = importlib.util.spec_from_file_location("gattn_c_abi_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    exe = mod.build(out=str(tmp_path / "gattn_c_roundtrip"))
+    assert os.access(exe, os.X_OK)
