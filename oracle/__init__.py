@@ -14,7 +14,9 @@ chain rule of that forward (the pages only say the model is trained with
 backprop); see the header of `gattn_ref.cpp` for the formulas.
 
 `oracle.dropout` adds attention dropout (float64 numpy, the mask drawn with
-the Philox generator of `oracle.philox`).
+the Philox generator of `oracle.philox`).  `oracle.rows` evaluates single
+query rows and key columns (float64 numpy) for sequences too long for the
+whole-problem oracle.
 """
 from __future__ import annotations
 

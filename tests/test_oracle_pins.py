@@ -277,3 +277,29 @@ def test_kv_forward_single_query_is_plain_softmax_attention():
     ref = np.einsum("bhj,bhjd->bhd", w / w.sum(-1, keepdims=True), v)
     assert np.allclose(o[:, :, 0], ref, rtol=1e-13, atol=1e-13)
     assert np.allclose(lse[:, :, 0], np.log(np.exp(s).sum(-1)), rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------- single rows and key columns (oracle.rows)
+@pytest.mark.parametrize("T,hs,scale", [(37, 16, 0.3), (64, 8, 1.1)])
+def test_rows_and_columns_equal_the_whole_problem_oracle(T, hs, scale):
+    """oracle.rows evaluates one query row (or one key column) at a time in
+    numpy, for sequences too long for the whole-problem oracle.  On small
+    problems every row's o, lse and dq and every key's dk and dv equal those of
+    the C++ oracle (pinned above) to float64 rounding, and a key range taken
+    from the middle equals the same keys of the whole problem."""
+    from oracle import rows
+    q, k, v, dO = (_rand((T, hs), 60 + i) for i in range(4))
+    dq, dk, dv, o, lse = oracle.attention_backward(q[None, None], k[None, None], v[None, None],
+                                                   dO[None, None], scale)
+    ro, rl = rows.forward_rows(q, k, v, scale, range(T))
+    np.testing.assert_allclose(ro, o[0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(rl, lse[0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(rows.dq_rows(q, k, v, dO, scale, range(T)), dq[0, 0], rtol=0,
+                               atol=1e-12)
+    rdk, rdv = rows.dkdv_columns(q, k, v, dO, scale, 0, T)
+    np.testing.assert_allclose(rdk, dk[0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(rdv, dv[0, 0], rtol=0, atol=1e-12)
+    j0, j1 = T // 3, T // 3 + 9
+    mdk, mdv = rows.dkdv_columns(q, k, v, dO, scale, j0, j1)
+    np.testing.assert_allclose(mdk, dk[0, 0, j0:j1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(mdv, dv[0, 0, j0:j1], rtol=0, atol=1e-12)
