@@ -29,14 +29,9 @@ FLAGS = [
 ]
 
 
-# Per-file extras.  The bf16 MFMA kernels are built assuming no NaN reaches
-# their arithmetic (NaN inputs are unspecified behaviour in the C ABI): this
-# lets the compiler fold the row maxima into v_max3_f32 instead of quieting
-# every MFMA result first.  The float32 path keeps full IEEE semantics.
-FILE_FLAGS = {
-    "mfma16_fwd.hip": ["-fno-honor-nans"],
-    "mfma16_bwd.hip": ["-fno-honor-nans"],
-}
+# Per-file extras (none at present: every kernel keeps IEEE NaN semantics, so
+# a NaN input reaches the outputs that depend on it).
+FILE_FLAGS: dict = {}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -106,6 +106,9 @@ __global__ __launch_bounds__(kThreads) void pre16_kernel(const uint16_t* __restr
 //   B(b): P, dS (f32, registers) -> 16-bit, exactly the B operand of
 //   C(b): dV^T += dO^T P, dK^T += Q^T dS   C[d][key]; dO^T, Q^T via LDS
 //                                          transpose reads
+// S and dK use fp16 operands (see DsOf): the Q tile is converted in place as
+// it lands, the K fragments once; dP and dV stay in the input type.  D is
+// the exact row term the dQ kernel wrote.
 // In the steps that meet the diagonal, blocks wholly before this wavefront's
 // keys are skipped and the others masked.
 //
@@ -147,7 +150,7 @@ __device__ __forceinline__ void dkdv_sdp(const uint16_t* Qb, const uint16_t* Gb,
   dp = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < C::KSTEP; ++ks) {
-    s = E::mfma(op_nat<HS>(Qb, L, qb * 32, ks), R.kf[ks], s);
+    s = DsOf<E>::T::mfma(op_nat<HS>(Qb, L, qb * 32, ks), R.kf[ks], s);
     dp = E::mfma(op_nat<HS>(Gb, L, qb * 32, ks), R.vf[ks], dp);
   }
 }
@@ -222,7 +225,7 @@ __device__ __forceinline__ void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       pp[t][e] = E::pack(pv[2 * e], pv[2 * e + 1]);
-      dsp[t][e] = E::pack(dsv[2 * e], dsv[2 * e + 1]);
+      dsp[t][e] = DsOf<E>::T::pack(dsv[2 * e], dsv[2 * e + 1]);
     }
   }
 #pragma unroll
@@ -231,7 +234,7 @@ __device__ __forceinline__ void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb
     for (int db = 0; db < C::DB; ++db) {
       const int k0 = qb * 32 + 16 * t;
       R.dva[db] = E::mfma(op_tr<HS>(Gb, L, k0, db), pp[t], R.dva[db]);
-      R.dka[db] = E::mfma(op_tr<HS>(Qb, L, k0, db), dsp[t], R.dka[db]);
+      R.dka[db] = DsOf<E>::T::mfma(op_tr<HS>(Qb, L, k0, db), dsp[t], R.dka[db]);
     }
 }
 
@@ -326,6 +329,7 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
     R.kf[ks] = bload16(rk, off);
     R.vf[ks] = bload16(rv, off);
   }
+
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) R.dka[db] = R.dva[db] = f32x16{};
 
@@ -345,10 +349,16 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
 #pragma unroll
   for (int j = 0; j < C::NS - 1; ++j)
     if (j < nsteps) issue(qt0 + j, j);
-  wait_ring<C::NS, C::PER>(min(C::NS - 2, nsteps - 1));
+  wait_ring<C::NS, C::PER>(min(C::NS - 2, nsteps - 1));  // also the K, V fragments
+  if constexpr (DsOf<E>::kConvert) {
+#pragma unroll
+    for (int ks = 0; ks < C::KSTEP; ++ks) R.kf[ks] = bf16x8_to_f16x8(R.kf[ks]);
+    dma_tile_to_f16<HS, C::BQ, C::NW>(Qs[0], w, lane);
+  }
   __syncthreads();
   // One step: prefetch step t+NS-1 into the buffer freed by step t-1, compute
-  // step t, wait until step t+1 has landed, publish.
+  // step t, wait until step t+1 has landed, convert this wavefront's part of
+  // its Q tile, publish.
   auto step = [&](int t, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     if (t + C::NS - 1 < nsteps) issue(qt0 + t + C::NS - 1, (buf + C::NS - 1) % C::NS);
@@ -360,6 +370,8 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
       dkdv_step_full<E, HS, DROP>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, krow, h, c, L, R,
                                   uint32_t(bh), dr);
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nsteps - t - 2)));
+    if constexpr (DsOf<E>::kConvert)
+      if (t + 1 < nsteps) dma_tile_to_f16<HS, C::BQ, C::NW>(Qs[(buf + 1) % C::NS], w, lane);
     __syncthreads();
   };
   ring_loop<C::NS>(nsteps, step);
@@ -385,15 +397,22 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
 // ---------------------------------------------------------------------------
 // dQ.  Workgroup = 4 wavefronts = 128 queries of one (b, h); wavefront w keeps
 // queries r0 + 32w .. +31 (Q^T and dO^T as MFMA B operands, lse and D as
-// per-lane scalars) and the dQ^T accumulator in registers.  It computes D
-// from its O and dO rows and writes D and lse*log2(e) to the workspace for
-// the dK/dV kernel.  Steps walk 64-key tiles from 0 to the diagonal.  Per
-// step and 32-key block:
+// per-lane scalars) and the dQ^T accumulator in registers.  Steps walk 64-key
+// tiles from 0 to the diagonal.  Per step and 32-key block:
 //   S^T = K Q^T, dP^T = V dO^T      C[key][query]; K, V rows from LDS in
 //                                   perm_row order (8 consecutive keys per
 //                                   lane in registers 8t..8t+7)
-//   dS^T (f32) -> 16-bit             the B operand of
+//   dS^T (f32) -> fp16               the B operand of
 //   dQ^T += K^T dS^T                 C[d][query]; K^T via LDS transpose reads
+// The walk starts from the row term D~ = rowsum(dO * O) of the stored 16-bit
+// O, which is off by up to half an ulp of each O element.  The exact row term
+// is D = sum_j P dP (sum_j P = 1), so with dS~ = P (dP - D~):
+//   eps = D - D~ = sum_j dS~,   dQ = scale (sum_j dS~ K - eps sum_j P K),
+// i.e. the kernel also accumulates M^T += K^T P^T (same K^T operands) and the
+// float32 row sums of dS~, and writes the exact D to the workspace for the
+// dK/dV kernel.  With dropout dS~ = P (Z dP - D~) and the same identities
+// hold (sum_j P Z dP = dO . O).  K and Q^T are fp16 (see DsOf): the K tile
+// is converted in place as it lands, Q^T once.
 template <int HS>
 struct DqCfg {
   static constexpr int NW = 4;
@@ -421,12 +440,14 @@ template <class E, int HS, int KIND, bool DROP>
 __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, int dn, float c,
                                         float lse2, float Dq, const LaneOffsets<HS>& L,
                                         const u32x4 (&qf)[HS / 16], const u32x4 (&gf)[HS / 16],
-                                        f32x16 (&dqa)[HS / 32], uint32_t qrow, uint32_t g0,
-                                        uint32_t bh, const Dropout& dr) {
+                                        f32x16 (&dqa)[HS / 32], f32x16 (&mka)[HS / 32],
+                                        float& esum, uint32_t qrow, uint32_t g0, uint32_t bh,
+                                        const Dropout& dr) {
   using C = DqCfg<HS>;
+  using Ed = typename DsOf<E>::T;
   constexpr int NKB = KIND == kDiagLo ? 1 : 2;  // 32-key blocks computed
   constexpr int KD = KIND == kDiagLo ? 0 : (KIND == kDiagHi ? 1 : -1);  // the diagonal block
-  u32x4 dsp[2][2];
+  u32x4 dsp[2][2], pp[2][2];
   // Keep bits of the step's runs, drawn before the S / dP MFMAs so that the
   // generator's vector ALU work overlaps them.
   uint32_t bits[2][2] = {{0xFFu, 0xFFu}, {0xFFu, 0xFFu}};
@@ -441,23 +462,28 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int ks = 0; ks < C::KSTEP; ++ks) {
-      st = E::mfma(op_nat<HS>(Kb, L, kb * 32, ks), qf[ks], st);
+      st = Ed::mfma(op_nat<HS>(Kb, L, kb * 32, ks), qf[ks], st);
       dpt = E::mfma(op_nat<HS>(Vb, L, kb * 32, ks), gf[ks], dpt);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      float dsv[8];
+      float pv[8], dsv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float p = __builtin_amdgcn_exp2f(fmaf(st[8 * t + e], c, -lse2));
         if (kb == KD && 16 * t + e > dn) p = 0.f;
+        pv[e] = p;
         if constexpr (DROP)
           dsv[e] = p * (keep_or_zero(dpt[8 * t + e] * dr.zs, bits[kb][t], e) - Dq);
         else
           dsv[e] = p * (dpt[8 * t + e] - Dq);
+        esum += dsv[e];
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dsp[kb][t][e] = E::pack(dsv[2 * e], dsv[2 * e + 1]);
+      for (int e = 0; e < 4; ++e) {
+        dsp[kb][t][e] = Ed::pack(dsv[2 * e], dsv[2 * e + 1]);
+        pp[kb][t][e] = Ed::pack(pv[2 * e], pv[2 * e + 1]);
+      }
     }
   }
 #pragma unroll
@@ -465,15 +491,18 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-        dqa[db] = E::mfma(op_tr<HS>(Kb, L, kb * 32 + 16 * t, db), dsp[kb][t], dqa[db]);
+      for (int db = 0; db < C::DB; ++db) {
+        const u32x4 kt = op_tr<HS>(Kb, L, kb * 32 + 16 * t, db);
+        dqa[db] = Ed::mfma(kt, dsp[kb][t], dqa[db]);
+        mka[db] = Ed::mfma(kt, pp[kb][t], mka[db]);
+      }
   // Scheduling hint: spread the MFMAs over the step, each followed by vector
   // ALU work and LDS reads of other blocks, instead of phase after phase.
 #pragma unroll
-  for (int i = 0; i < NKB * (2 * C::KSTEP + 2 * C::DB); ++i) {
+  for (int i = 0; i < NKB * (2 * C::KSTEP + 4 * C::DB); ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
 }
 
@@ -518,7 +547,7 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
     if (j < nkt) issue(j, j);
 
   // Q^T, dO^T fragments (lane (n, h): row qrow, columns 16 ks + 8h .. +7), and
-  // D = rowsum(dO * O) of this lane's query from the same columns of O.
+  // D~ = rowsum(dO * O) of this lane's query from the same columns of O.
   u32x4 qf[C::KSTEP], gf[C::KSTEP];
   float dpart = 0.f;
 #pragma unroll
@@ -537,19 +566,22 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
   const float Dq = halves_sum(dpart);
   const float lse2 = bloadf(make_rsrc(lse + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4) *
                      kLog2e;
-  if (h == 0) {
-    bstoref(make_rsrc(Dg + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4, Dq);
-    bstoref(make_rsrc(L2g + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4, lse2);
-  }
-  f32x16 dqa[C::DB];
+  if constexpr (DsOf<E>::kConvert) {
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) dqa[db] = f32x16{};
+    for (int ks = 0; ks < C::KSTEP; ++ks) qf[ks] = bf16x8_to_f16x8(qf[ks]);
+  }
+  f32x16 dqa[C::DB], mka[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) dqa[db] = mka[db] = f32x16{};
+  float esum = 0.f;
 
   const LaneOffsets<HS> L(lane);
   wait_vmem();  // the first tile and this wavefront's q, dO, O, lse rows
+  if constexpr (DsOf<E>::kConvert) dma_tile_to_f16<HS, C::BN, C::NW>(Ks[0], w, lane);
   __syncthreads();
   // One step: prefetch key tile kt+NS-1 into the buffer freed by tile kt-1,
-  // compute tile kt, wait until tile kt+1 has landed, publish.
+  // compute tile kt, wait until tile kt+1 has landed, convert this
+  // wavefront's part of its K tile, publish.
   auto step = [&](int kt, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     if (kt + C::NS - 1 < nkt) issue(kt + C::NS - 1, (buf + C::NS - 1) % C::NS);
@@ -557,31 +589,40 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
     const uint32_t g0 = uint32_t(key0 / 8 + h), ub = uint32_t(bh), uq = uint32_t(qrow);
     if (q0 < T && key0 <= q0) {
       if (key0 == q0)
-        dq_step<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, uq, g0,
-                                      ub, dr);
+        dq_step<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
+                                      uq, g0, ub, dr);
       else if (key0 + 32 == q0)
-        dq_step<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, uq, g0,
-                                      ub, dr);
+        dq_step<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
+                                      uq, g0, ub, dr);
       else
-        dq_step<E, HS, kFull, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, uq, g0, ub,
-                                    dr);
+        dq_step<E, HS, kFull, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
+                                    uq, g0, ub, dr);
     }
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
+    if constexpr (DsOf<E>::kConvert)
+      if (kt + 1 < nkt) dma_tile_to_f16<HS, C::BN, C::NW>(Ks[(buf + 1) % C::NS], w, lane);
     __syncthreads();
   };
   ring_loop<C::NS>(nkt, step);
 
+  // eps = D - D~ (both halves of the wavefront hold this query's keys).
   // dQ^T register i of lane (n, h): column d = db*32 + 8*(i/4) + 4h + i%4, query qrow.
+  const float eps = halves_sum(esum);
+  if (h == 0) {
+    bstoref(make_rsrc(Dg + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4, Dq + eps);
+    bstoref(make_rsrc(L2g + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4, lse2);
+  }
   const rsrc_t wq = make_rsrc(dq + slice_base<HS, STRIDED>(lg, bh, H, T),
                               slice_bytes_of<HS, STRIDED>(lg, T));
   const int rsg = STRIDED ? int(lg.st) : HS;
+  auto fin = [&](int db, int i) { return fmaf(-eps, mka[db][i], dqa[db][i]) * scale; };
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t off = uint32_t(qrow * rsg + db * 32 + 8 * g + 4 * h) * 2;
-      bstore8(wq, off, u32x2{E::pack(dqa[db][4 * g] * scale, dqa[db][4 * g + 1] * scale),
-                             E::pack(dqa[db][4 * g + 2] * scale, dqa[db][4 * g + 3] * scale)});
+      bstore8(wq, off, u32x2{E::pack(fin(db, 4 * g), fin(db, 4 * g + 1)),
+                             E::pack(fin(db, 4 * g + 2), fin(db, 4 * g + 3))});
     }
 }
 

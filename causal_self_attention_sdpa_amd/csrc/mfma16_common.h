@@ -72,6 +72,27 @@ struct F16 {
   __device__ static float hi(uint32_t w) { return float(__builtin_bit_cast(f16x2, w)[1]); }
 };
 
+// Element type of the backward's dS products (dQ = scale dS K, dK = scale
+// dS^T Q, and the row-term correction P K): fp16 for both 16-bit types.
+// dS rounded to bf16 (8 significant bits) moves dQ and dK by up to
+// 2^-9 |dS| |K| per term, which for inputs of twice unit variance already
+// exceeds 2e-2 + 2^-8 |ref|; fp16 keeps 11 bits.  The other operand (K or Q)
+// is then needed in fp16 too: for bf16 inputs it is converted, exactly for
+// magnitudes in [2^-14, 65504] (smaller ones keep 2^-24 absolute precision
+// as fp16 subnormals, larger ones become inf), and dS must stay below 65504.
+template <class E>
+struct DsOf {
+  using T = F16;
+  static constexpr bool kConvert = !std::is_same<E, F16>::value;
+};
+
+// Packed bf16 pair -> packed fp16 pair (round to nearest even).
+__device__ inline uint32_t bf16x2_to_f16x2(uint32_t w) { return F16::pack(bf16lo(w), bf16hi(w)); }
+__device__ inline u32x4 bf16x8_to_f16x8(const u32x4& x) {
+  return u32x4{bf16x2_to_f16x2(x[0]), bf16x2_to_f16x2(x[1]), bf16x2_to_f16x2(x[2]),
+               bf16x2_to_f16x2(x[3])};
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -211,6 +232,21 @@ __device__ inline void dma_tile(rsrc_t r, int row0, int st, uint16_t* tile, int 
     const uint32_t off = uint32_t((row0 + rl) * st + c * 8) * 2;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)(tile + i * 512), 16, off, 0, 0, 0);
+  }
+}
+// Converts, in place, the bf16 chunks of a tile that this wavefront's own
+// dma_tile<HS, ROWS, NW> instructions wrote (lane L of instruction i: the 16
+// bytes at element i*512 + 8L) to fp16.  Call after the wavefront's own wait
+// for that DMA and before the barrier that publishes the tile: the chunks
+// converted are exactly the ones this wavefront's wait covers, so the whole
+// tile is fp16 once every wavefront has passed the barrier.
+template <int HS, int ROWS, int NW>
+__device__ inline void dma_tile_to_f16(uint16_t* tile, int w, int lane) {
+  constexpr int NI = ROWS * HS / 512;
+#pragma unroll
+  for (int i = w; i < NI; i += NW) {
+    u32x4* p = reinterpret_cast<u32x4*>(tile + i * 512 + 8 * lane);
+    *p = bf16x8_to_f16x8(*p);
   }
 }
 // DMA of n32 4-byte values (n32 <= 64) from byte offset off0 of a resource

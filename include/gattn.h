@@ -30,7 +30,12 @@
  * Dtypes: q, k, v, o, dO, dq, dk, dv all have `dtype`; lse is always float32.
  *   GATTN_BF16: hs in {32, 64}; MFMA kernels, bf16 inputs/outputs, float32
  *               accumulation, every float32 -> bf16 conversion rounds to
- *               nearest even.
+ *               nearest even.  The backward's dS products (dq = scale dS k,
+ *               dk = scale dS^T q) take fp16 operands: dS keeps 11
+ *               significant bits instead of bf16's 8, and q and k are
+ *               converted to fp16, exactly for magnitudes in
+ *               [2^-14, 65504] (smaller ones keep 2^-24 absolute precision,
+ *               larger ones become inf); |dS| must stay below 65504.
  *   GATTN_F16 : IEEE binary16 (the pages' other half-precision option), same
  *               kernels and rules as GATTN_BF16 with the fp16 MFMA; the
  *               softmax weights stay <= 256 and are stored to fp16 only as
@@ -152,7 +157,10 @@ size_t gattn_bwd_workspace_bytes(int B, int H, int T, int hs, int dtype);
 
 /*
  * Backward: dq, dk, dv of L = sum(dO * o) for the forward above (chain rule;
- * the pages state only that training runs a backward pass).
+ * the pages state only that training runs a backward pass).  The row term
+ * D[i] is the exact sum_j P[i][j] dP[i][j] (= dO[i] . o[i] before o was
+ * rounded to `dtype`): the dQ pass starts from dO . o of the stored o and
+ * corrects it, and dq, by the float32 row sums of dS.
  *   q, k, v, o, dO : inputs (B, H, T, hs), `dtype`; o is what gattn_fwd wrote.
  *   lse            : input (B, H, T) float32, what gattn_fwd wrote (required).
  *   dq, dk, dv     : outputs (B, H, T, hs), `dtype`.
@@ -184,9 +192,11 @@ int gattn_bwd_strided(const void* q, const void* k, const void* v, const void* o
                       hipStream_t stream);
 
 /*
- * Backward, row terms only: D[i] = sum_d dO[i][d] * o[i][d] (the row term of
- * dS = P (dP - D)) and lse[i] * log2(e), float32, into the workspace.  Needed
- * before gattn_bwd_dkdv when gattn_bwd_dq is not run first.
+ * Backward, row terms only: D[i] = sum_d dO[i][d] * o[i][d] from the stored o
+ * (the row term of dS = P (dP - D), off by up to half an ulp of each o
+ * element; gattn_bwd_dq writes it exactly) and lse[i] * log2(e), float32,
+ * into the workspace.  For callers that run gattn_bwd_dkdv without
+ * gattn_bwd_dq first.
  */
 int gattn_bwd_preprocess(const void* o, const void* dO, const float* lse, int B, int H, int T,
                          int hs, int dtype, void* workspace, size_t workspace_bytes,
@@ -194,8 +204,8 @@ int gattn_bwd_preprocess(const void* o, const void* dO, const float* lse, int B,
 
 /*
  * Backward, dq = scale * dS k, with P recomputed from q, k and lse (exactly 0
- * above the diagonal) and dS = P (dO v^T - D).  Also leaves the row terms of
- * gattn_bwd_preprocess in the workspace.
+ * above the diagonal) and dS = P (dO v^T - D).  Also leaves the row terms in
+ * the workspace, D exact (see gattn_bwd).
  */
 int gattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, void* dq, int B, int H, int T, int hs, float scale, int dtype,
@@ -204,7 +214,8 @@ int gattn_bwd_dq(const void* q, const void* k, const void* v, const void* o, con
 /*
  * Backward, dk = scale * dS^T q and dv = P^T dO, recomputing P and dS as
  * gattn_bwd_dq does from the row terms already in the workspace (written by
- * gattn_bwd_dq or gattn_bwd_preprocess earlier on the stream).
+ * gattn_bwd_dq, exact, or gattn_bwd_preprocess earlier on the stream).
+ * gattn_bwd_dq then gattn_bwd_dkdv equals gattn_bwd bit for bit.
  */
 int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, void* dk,
                    void* dv, int B, int H, int T, int hs, float scale, int dtype, void* workspace,

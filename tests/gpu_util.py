@@ -22,8 +22,12 @@ def to_dev(a: np.ndarray, dtype: str):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch_dtype(dtype))
 
 
-def gpu_fwd_bwd(x: dict, dtype: str, scale: float, use_stages: bool = False):
-    """Runs gattn_fwd then gattn_bwd; returns float64 numpy (dq, dk, dv, o, lse)."""
+def gpu_fwd_bwd(x: dict, dtype: str, scale: float, use_stages: bool = False,
+                preprocess: bool = False):
+    """Runs gattn_fwd then gattn_bwd; returns float64 numpy (dq, dk, dv, o, lse).
+    use_stages: the backward as its two stages, gattn_bwd_dq then
+    gattn_bwd_dkdv.  preprocess: the row terms from gattn_bwd_preprocess
+    (D from the stored o), then gattn_bwd_dkdv, then gattn_bwd_dq."""
     import torch
     import causal_self_attention_sdpa_amd as ga
     t = {n: to_dev(a, dtype) for n, a in x.items()}
@@ -35,12 +39,13 @@ def gpu_fwd_bwd(x: dict, dtype: str, scale: float, use_stages: bool = False):
     ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, code), dtype=torch.uint8,
                      device="cuda")
     dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
-    if use_stages:
-        # row terms from the preprocess stage, dk/dv first, then dq (which
-        # rewrites the same row terms)
+    if preprocess:
         ga.gattn_bwd_preprocess(o, t["do"], lse, ws)
         ga.gattn_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], dk, dv, scale, ws)
         ga.gattn_bwd_dq(t["q"], t["k"], t["v"], o, t["do"], lse, dq, scale, ws)
+    elif use_stages:
+        ga.gattn_bwd_dq(t["q"], t["k"], t["v"], o, t["do"], lse, dq, scale, ws)
+        ga.gattn_bwd_dkdv(t["q"], t["k"], t["v"], t["do"], dk, dv, scale, ws)
     else:
         ga.gattn_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, dq, dk, dv, scale, ws)
     torch.cuda.synchronize()
@@ -85,21 +90,23 @@ U_F16 = 2.0 ** -11  # unit roundoff of IEEE binary16 (11 significant bits)
 
 
 def rounding_bound(x: dict, scale: float, slices, ref, u: float = U_BF16, slack: float = 1e-3,
-                   z=None):
+                   z=None, u_ds: float = U_F16):
     """First-order bound on the error of a 16-bit path, per element, for the
     selected (b, h) slices, derived from where that path rounds:
-      o  = P V           P rounded to bf16 before the MFMA
-      dv = P^T dO        P rounded
-      dk = s dS^T Q      dS rounded; D = rowsum(dO * O) uses the bf16-stored O
-      dq = s dS K        same
-    plus the rounding of the stored bf16 output itself (u |ref|).  Terms are
+      o  = P V           P rounded to the input type (u) before the MFMA
+      dv = P^T dO        P rounded (u)
+      dk = s dS^T Q      dS rounded to fp16 (u_ds), with the exact row term D
+      dq = s dS~ K       dS~ = P (dP - D~) rounded to fp16, D~ from the
+                         16-bit-stored O (off by at most u sum |dO| |O|), and
+                         the float32 correction s (D - D~) P K
+    plus the rounding of the stored output itself (u |ref|).  Terms are
     float64 magnitudes built from the inputs and the oracle's lse:
-    |err| <= u (|ref| + Mag) + slack with Mag = sum of |operand products|; u
-    is the unit roundoff of the 16-bit type (bf16 2^-8, fp16 2^-11), `slack`
-    covers the float32 arithmetic (and is the whole bound of lse, which is
-    never rounded to 16 bits).  With attention dropout, z (n, T, T) holds the
-    weight multipliers of each selected slice: P Z takes P's place in o and
-    dv, and dS = P (Z dP - D)."""
+    |err| <= u |ref| + u_o Mag + slack with Mag = sum of |operand products|
+    (u_o = u for o and dv, u_ds for dq and dk); u is the unit roundoff of the
+    16-bit type (bf16 2^-8, fp16 2^-11), `slack` covers the float32 arithmetic
+    (and is the whole bound of lse, which is never rounded to 16 bits).  With
+    attention dropout, z (n, T, T) holds the weight multipliers of each
+    selected slice: P Z takes P's place in o and dv, and dS = P (Z dP - D)."""
     sel = {n: np.stack([a[b, h] for b, h in slices]) for n, a in x.items()}
     dq_r, dk_r, dv_r, o_r, lse_r = (a[:, 0] for a in ref)
     T = sel["q"].shape[1]
@@ -111,19 +118,19 @@ def rounding_bound(x: dict, scale: float, slices, ref, u: float = U_BF16, slack:
     D = np.sum(sel["do"] * o_r, axis=-1)
     dP = np.einsum("nid,njd->nij", sel["do"], sel["v"])
     dS = P * (Z * dP - D[:, :, None])
-    W = np.abs(dS) + P * A[:, :, None]
+    W = np.abs(dS) + u * P * A[:, :, None]  # |dS~|
     mag = {
-        "o": (P * Z) @ np.abs(sel["v"]),
-        "dv": np.swapaxes(P * Z, 1, 2) @ np.abs(sel["do"]),
-        "dk": scale * np.swapaxes(W, 1, 2) @ np.abs(sel["q"]),
-        "dq": scale * W @ np.abs(sel["k"]),
+        "o": u * ((P * Z) @ np.abs(sel["v"])),
+        "dv": u * (np.swapaxes(P * Z, 1, 2) @ np.abs(sel["do"])),
+        "dk": u_ds * scale * (np.swapaxes(np.abs(dS), 1, 2) @ np.abs(sel["q"])),
+        "dq": u_ds * scale * (W @ np.abs(sel["k"])),
     }
     out = []
     for n, r in zip(OUT_NAMES, (dq_r, dk_r, dv_r, o_r, lse_r)):
         if n == "lse":
             out.append(np.full(r.shape, slack)[:, None])
         else:
-            out.append((u * (np.abs(r) + mag[n]) + slack)[:, None])
+            out.append((u * np.abs(r) + mag[n] + slack)[:, None])
     return tuple(out)
 
 

@@ -1,9 +1,12 @@
 """GPU backward metamorphic checks through the C ABI (bf16 path).
 
-dk and dv are produced without atomics, so they are bit-deterministic and the
-exact properties below are checked bit for bit.  dq is accumulated with float32
-atomics in an order that can change between runs, so its checks use a
-tolerance."""
+No kernel uses atomics: dq (the dQ kernel, one workgroup per query tile) and
+dk, dv (the dK/dV kernel, one workgroup per key tile) each come from a fixed
+order of operations, so determinism, causality and the head split are checked
+bit for bit; a race or a lost or repeated tile in either kernel breaks one of
+them.  Scaling V by 2 scales dS by 2, and dS enters the dq and dk products as
+fp16, whose subnormal range (|dS| < 2^-14) rounds on a fixed grid that does
+not scale: there dq and dk x 2 are held to one bf16 ulp, dv bit for bit."""
 import numpy as np
 import pytest
 
@@ -45,8 +48,7 @@ def dev_inputs(B, H, T, hs, seed):
 @pytest.mark.parametrize("hs", [64, 32])
 def test_bwd_causality(hs):
     """Changing rows < j of q and dO leaves dk, dv rows >= j bit-identical;
-    changing rows > i of q, k, v, dO leaves dq rows <= i unchanged (within
-    the atomics' reordering)."""
+    changing rows > i of q, k, v, dO leaves dq rows <= i bit-identical."""
     import torch
     T = 333
     t = dev_inputs(2, 2, T, hs, 31)
@@ -66,13 +68,13 @@ def test_bwd_causality(hs):
         for n in p:
             p[n][:, :, i + 1:] = p[n][:, :, i + 1:] * 3 - 1
         dq1, _, _ = run(p, s)
-        err = (dq0[:, :, :i + 1].float() - dq1[:, :, :i + 1].float()).abs().max().item()
-        assert err <= 2e-2, (i, err)
+        assert torch.equal(dq0[:, :, :i + 1], dq1[:, :, :i + 1]), i
 
 
 def test_bwd_value_scaling():
-    """V x 2: dv unchanged and dk x 2, bit for bit (power-of-two scaling
-    commutes with every rounding); dq x 2 within the atomics' reordering."""
+    """V x 2: dv unchanged bit for bit; dk x 2 and dq x 2 to one bf16 ulp
+    (power-of-two scaling commutes with every rounding except that of fp16
+    subnormal dS values)."""
     import torch
     t = dev_inputs(2, 3, 290, 64, 32)
     s = default_scale(64)
@@ -81,24 +83,26 @@ def test_bwd_value_scaling():
     t2["v"] = t["v"] * 2
     dq1, dk1, dv1 = run(t2, s)
     assert torch.equal(dv1, dv0)
-    assert torch.equal(dk1, dk0 * 2)
-    assert (dq1.float() - 2 * dq0.float()).abs().max().item() <= 2e-2
+    for a, b in ((dk1, dk0 * 2), (dq1, dq0 * 2)):
+        a, b = a.float(), b.float()
+        assert torch.all((a - b).abs() <= b.abs() * 2.0 ** -7 + 1e-6)
+        assert (a != b).float().mean().item() < 0.01
 
 
-def test_bwd_deterministic_dk_dv():
+def test_bwd_deterministic():
     import torch
     t = dev_inputs(3, 4, 777, 64, 33)
     s = default_scale(64)
     a = run(t, s)
     b = run(t, s)
-    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
-    assert (a[0].float() - b[0].float()).abs().max().item() <= 1e-2
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
     for x in a:
         assert torch.isfinite(x).all()
 
 
 def test_bwd_heads_split():
-    """25 heads in one call: dk, dv equal the single-head calls bit for bit."""
+    """25 heads in one call: dq, dk, dv equal the single-head calls bit for bit."""
     import torch
     t = dev_inputs(1, 25, 200, 64, 34)
     s = default_scale(64)
@@ -107,7 +111,7 @@ def test_bwd_heads_split():
         th = {n: a[:, h:h + 1].contiguous() for n, a in t.items()}
         dqh, dkh, dvh = run(th, s)
         assert torch.equal(dkh, dk[:, h:h + 1]) and torch.equal(dvh, dv[:, h:h + 1]), h
-        assert (dqh.float() - dq[:, h:h + 1].float()).abs().max().item() <= 1e-2
+        assert torch.equal(dqh, dq[:, h:h + 1]), h
 
 
 def test_bwd_guard_bands_and_poison():
@@ -130,4 +134,4 @@ def test_bwd_guard_bands_and_poison():
         assert torch.all(b[:pad] == 7.0) and torch.all(b[pad + n:] == 7.0)
         assert torch.isfinite(vw).all()
     ref = run(t, s)
-    assert torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])
+    assert torch.equal(dq, ref[0]) and torch.equal(dk, ref[1]) and torch.equal(dv, ref[2])

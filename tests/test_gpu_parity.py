@@ -3,15 +3,15 @@ by element, on the same seeded inputs.
 
 Bars (every element of o, lse, dq, dk, dv):
   * f32 path: max-abs 1e-4;
-  * bf16 path with unit-variance inputs (and the x0.5 variant):
-    |err| <= 2e-2 + 2^-8 |ref|: the 2e-2 max-abs bar plus the rounding of the
-    stored bf16 value itself (half an ulp, up to 2^-8 |ref|; 0.0156 for
-    values in [4, 8), where gradients of unit-variance inputs do land);
-  * bf16 with inputs x2.0 (softmax-range stress, no longer unit variance):
-    the first-order rounding bound of gpu_util.rounding_bound, derived from
-    where the path rounds to bf16 (P, dS, the stored O and the outputs).
-Small shapes are checked in full; full-size shapes on sampled (b, h) slices,
-each slice computed independently by the oracle.
+  * bf16 path, unit-variance inputs, the x0.5 variant and the x2.0 stress
+    variant of the GPT-2 124M shape: |err| <= 2e-2 + 2^-8 |ref|: the 2e-2
+    max-abs bar plus the rounding of the stored bf16 value itself (half an
+    ulp, up to 2^-8 |ref|; 0.0156 for values in [4, 8), where gradients of
+    unit-variance inputs do land, 0.031 in [8, 16), where the x2.0 ones do).
+Small shapes are checked in full; every (b, h) slice of one layer of the
+char-level and GPT-2 124M shapes against the whole-layer oracle; other
+full-size layers on sampled (b, h) slices, each slice computed independently
+by the oracle.  The raw max-abs error of each output is printed.
 """
 import math
 
@@ -37,11 +37,12 @@ def _gpu():
     ga.load_library()
 
 
-def _full(B, H, T, hs, dtype, tol, rel=0.0, qkv_scale=1.0, seed=1234, stages=False):
+def _full(B, H, T, hs, dtype, tol, rel=0.0, qkv_scale=1.0, seed=1234, stages=False,
+          preprocess=False):
     x = inputs(B, H, T, hs, dtype, seed=seed, qkv_scale=qkv_scale)
     s = default_scale(hs)
     print(f"case {dtype} B={B} H={H} T={T} hs={hs} x{qkv_scale} seed={seed}", flush=True)
-    got = gpu_fwd_bwd(x, dtype, s, use_stages=stages)
+    got = gpu_fwd_bwd(x, dtype, s, use_stages=stages, preprocess=preprocess)
     import oracle
     ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], s)
     return check_close(got, ref, tol, rel, where=f"{dtype} {(B, H, T, hs)}")
@@ -84,7 +85,21 @@ def test_bf16_several_tiles_full_check():
 
 
 def test_bf16_stages_equal_composite():
+    """gattn_bwd_dq then gattn_bwd_dkdv is gattn_bwd, bit for bit."""
+    x = inputs(1, 3, 190, 64, "bf16", seed=1234)
+    s = default_scale(64)
+    a = gpu_fwd_bwd(x, "bf16", s)
+    b = gpu_fwd_bwd(x, "bf16", s, use_stages=True)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
     _full(1, 3, 190, 64, "bf16", BF16_TOL, BF16_REL, stages=True)
+
+
+@pytest.mark.parametrize("hs", [64, 32])
+def test_bf16_preprocess_then_dkdv(hs):
+    """Row terms from gattn_bwd_preprocess (D from the stored o), then dk/dv,
+    then dq (which rewrites the row terms exactly): within the bar."""
+    _full(2, 3, 300, hs, "bf16", BF16_TOL, BF16_REL, preprocess=True, seed=77)
 
 
 def test_bf16_char_level_reduced_batch():
@@ -102,13 +117,49 @@ def _sampled(B, H, T, hs, qkv_scale, slices, seed, layer=0, bound=False):
     x = inputs(B, H, T, hs, "bf16", seed=seed, layer=layer, qkv_scale=qkv_scale,
                workload=f"b{B}h{H}t{T}d{hs}")
     s = default_scale(hs)
-    print(f"case bf16 full-size B={B} H={H} T={T} hs={hs} x{qkv_scale} slices={slices}", flush=True)
+    print(f"case bf16 full-size B={B} H={H} T={T} hs={hs} x{qkv_scale} layer={layer} "
+          f"slices={slices}", flush=True)
     got = pick(gpu_fwd_bwd(x, "bf16", s), slices)
     ref = oracle_slices(x, s, slices)
-    where = f"bf16 {(B, H, T, hs)} x{qkv_scale}"
+    where = f"bf16 {(B, H, T, hs)} x{qkv_scale} layer {layer}"
     if bound:
         return check_bound(got, ref, rounding_bound(x, s, slices, ref), where=where)
-    return check_close(got, ref, BF16_TOL, BF16_REL, where=where)
+    rep = check_close(got, ref, BF16_TOL, BF16_REL, where=where)
+    print(f"  max abs err {where}: " + ", ".join(f"{n} {e:.4g}" for n, e in rep.items()),
+          flush=True)
+    return rep
+
+
+def _whole_layer(B, H, T, hs, qkv_scale, seed, layer=0):
+    """Every (b, h) slice of one layer against the whole-layer oracle."""
+    import oracle
+    x = inputs(B, H, T, hs, "bf16", seed=seed, layer=layer, qkv_scale=qkv_scale,
+               workload=f"b{B}h{H}t{T}d{hs}")
+    s = default_scale(hs)
+    where = f"bf16 {(B, H, T, hs)} x{qkv_scale} layer {layer} every slice"
+    print(f"case {where}", flush=True)
+    got = gpu_fwd_bwd(x, "bf16", s)
+    ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], s)
+    rep = check_close(got, ref, BF16_TOL, BF16_REL, where=where)
+    print(f"  max abs err {where}: " + ", ".join(f"{n} {e:.4g}" for n, e in rep.items()),
+          flush=True)
+    names = ("dq", "dk", "dv", "o", "lse")
+    n_flat = {n: int(np.sum(np.abs(g - r) > BF16_TOL)) for n, g, r in zip(names, got, ref)}
+    worst = {n: round(float(np.max(np.abs(g - r) / (BF16_TOL + BF16_REL * np.abs(r)))), 3)
+             for n, g, r in zip(names, got, ref)}
+    print(f"  elements above the flat 2e-2: {n_flat}; worst err / bar: {worst}", flush=True)
+    return rep
+
+
+def test_bf16_char_level_whole_layer():
+    """B=64, H=6, T=256, hs=64: all 384 slices of layer 0."""
+    _whole_layer(64, 6, 256, 64, 1.0, 1)
+
+
+@pytest.mark.parametrize("qkv_scale", [0.5, 2.0])
+def test_bf16_gpt2_small_whole_layer(qkv_scale):
+    """B=12, H=12, T=1024, hs=64, q/k/v x0.5 and x2.0: all 144 slices of layer 0."""
+    _whole_layer(12, 12, 1024, 64, qkv_scale, 2)
 
 
 def test_bf16_char_level_full_size():
@@ -122,8 +173,8 @@ def test_bf16_gpt2_small_half_scale():
 
 
 def test_bf16_gpt2_small_double_scale():
-    """Same shape, q/k/v x2.0: stress of the softmax range (rounding bound)."""
-    _sampled(12, 12, 1024, 64, 2.0, [(0, 0), (6, 4), (11, 11)], 2, bound=True)
+    """Same shape, q/k/v x2.0: stress of the softmax range, same bar."""
+    _sampled(12, 12, 1024, 64, 2.0, [(0, 0), (6, 4), (11, 11)], 2)
 
 
 def test_bf16_gpt2_xl_heads():
@@ -172,9 +223,10 @@ def test_bf16_narrow_heads_every_layer(T):
         check_close(got, ref, BF16_TOL, BF16_REL, where=f"bf16 {(B, H, T, hs)} layer {layer}")
 
 
+@pytest.mark.parametrize("qkv_scale", [0.5, 2.0])
 @pytest.mark.parametrize("layer", range(12))
-def test_bf16_gpt2_small_every_layer(layer):
-    _sampled(12, 12, 1024, 64, 0.5, _layer_slices(12, 12, layer), 2, layer=layer)
+def test_bf16_gpt2_small_every_layer(layer, qkv_scale):
+    _sampled(12, 12, 1024, 64, qkv_scale, _layer_slices(12, 12, layer), 2, layer=layer)
 
 
 @pytest.mark.parametrize("layer", [0, 23, 47])
