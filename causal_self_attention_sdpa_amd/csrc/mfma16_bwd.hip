@@ -40,9 +40,6 @@
 #ifndef GATTN_DKDV_STAGES
 #define GATTN_DKDV_STAGES 2
 #endif
-#ifndef GATTN_DQ_STAGES
-#define GATTN_DQ_STAGES 2
-#endif
 #ifndef GATTN_DKDV_OCC
 #define GATTN_DKDV_OCC 2
 #endif
@@ -420,7 +417,7 @@ struct DqCfg {
   static constexpr int BN = 64;       // keys per step
   static constexpr int KSTEP = HS / 16;
   static constexpr int DB = HS / 32;
-  static constexpr int NS = GATTN_DQ_STAGES;  // LDS ring depth
+  static constexpr int NS = 3;  // LDS ring depth: tile t computes while t+1 converts and t+2 lands
   static constexpr int PER = 2 * (BN * HS / 512) / NW;  // DMA instructions per wavefront per step
   static_assert((BN * HS / 512) % NW == 0, "uniform DMA split");
 };
@@ -436,13 +433,16 @@ struct DqCfg {
 // block, as in the forward.
 enum DqTile { kFull = 0, kDiagLo = 1, kDiagHi = 2 };
 
-template <class E, int HS, int KIND, bool DROP>
+// `between` runs once the first block's S and dP MFMAs are issued (the ring's
+// DMA issue and tile conversion, which then overlap the matrix core's work).
+template <class E, int HS, int KIND, bool DROP, class F>
 __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, int dn, float c,
                                         float lse2, float Dq, const LaneOffsets<HS>& L,
                                         const u32x4 (&qf)[HS / 16], const u32x4 (&gf)[HS / 16],
                                         f32x16 (&dqa)[HS / 32], f32x16 (&mka)[HS / 32],
-                                        float& esum, uint32_t qrow, uint32_t g0, uint32_t bh,
-                                        const Dropout& dr) {
+                                        float& esum, const f32x16& negD, uint32_t qrow,
+                                        uint32_t g0, uint32_t bh, const Dropout& dr,
+                                        F&& between) {
   using C = DqCfg<HS>;
   using Ed = typename DsOf<E>::T;
   constexpr int NKB = KIND == kDiagLo ? 1 : 2;  // 32-key blocks computed
@@ -459,11 +459,18 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    f32x16 st = {}, dpt = {};
+    // Without dropout the dP accumulator starts from -D~ (every register of
+    // a lane is this lane's query), so it ends as dP - D~.
+    f32x16 st = {}, dpt = DROP ? f32x16{} : negD;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEP; ++ks) {
       st = Ed::mfma(op_nat<HS>(Kb, L, kb * 32, ks), qf[ks], st);
       dpt = E::mfma(op_nat<HS>(Vb, L, kb * 32, ks), gf[ks], dpt);
+    }
+    if (kb == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      between();
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -476,13 +483,14 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
         if constexpr (DROP)
           dsv[e] = p * (keep_or_zero(dpt[8 * t + e] * dr.zs, bits[kb][t], e) - Dq);
         else
-          dsv[e] = p * (dpt[8 * t + e] - Dq);
+          dsv[e] = p * dpt[8 * t + e];
         esum += dsv[e];
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         dsp[kb][t][e] = Ed::pack(dsv[2 * e], dsv[2 * e + 1]);
         pp[kb][t][e] = Ed::pack(pv[2 * e], pv[2 * e + 1]);
+
       }
     }
   }
@@ -498,12 +506,7 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
       }
   // Scheduling hint: spread the MFMAs over the step, each followed by vector
   // ALU work and LDS reads of other blocks, instead of phase after phase.
-#pragma unroll
-  for (int i = 0; i < NKB * (2 * C::KSTEP + 4 * C::DB); ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
+
 }
 
 template <class E, int HS, bool STRIDED, bool DROP>  // STRIDED, DROP as for the dK/dV kernel
@@ -542,9 +545,7 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
     dma_tile<HS, C::BN, C::NW>(rv, kt * C::BN, rs, Vs[buf], w, lane);
   };
   const int nkt = (min(r0 + C::BM, T) - 1) / C::BN + 1;
-#pragma unroll
-  for (int j = 0; j < C::NS - 1; ++j)
-    if (j < nkt) issue(j, j);
+  issue(0, 0);
 
   // Q^T, dO^T fragments (lane (n, h): row qrow, columns 16 ks + 8h .. +7), and
   // D~ = rowsum(dO * O) of this lane's query from the same columns of O.
@@ -563,9 +564,10 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
       dpart = fmaf(E::hi(of[e]), E::hi(gf[ks][e]), dpart);
     }
   }
-  const float Dq = halves_sum(dpart);
   const float lse2 = bloadf(make_rsrc(lse + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4) *
                      kLog2e;
+  if (1 < nkt) issue(1, 1);
+  const float Dq = halves_sum(dpart);
   if constexpr (DsOf<E>::kConvert) {
 #pragma unroll
     for (int ks = 0; ks < C::KSTEP; ++ks) qf[ks] = bf16x8_to_f16x8(qf[ks]);
@@ -574,33 +576,48 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) dqa[db] = mka[db] = f32x16{};
   float esum = 0.f;
+  f32x16 negD;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negD[i] = -Dq;
 
   const LaneOffsets<HS> L(lane);
-  wait_vmem();  // the first tile and this wavefront's q, dO, O, lse rows
+  // Tile 0 and this wavefront's q, dO, O, lse rows (tile 1's DMA, issued
+  // last, may still be in flight).
+  if (1 < nkt)
+    wait_vmem_n<C::PER>();
+  else
+    wait_vmem();
   if constexpr (DsOf<E>::kConvert) dma_tile_to_f16<HS, C::BN, C::NW>(Ks[0], w, lane);
   __syncthreads();
-  // One step: prefetch key tile kt+NS-1 into the buffer freed by tile kt-1,
-  // compute tile kt, wait until tile kt+1 has landed, convert this
-  // wavefront's part of its K tile, publish.
+  // One step, tile kt in buffer kt % 3 (landed, converted and published by
+  // the previous barrier): wait for this wavefront's DMA of tile kt+1 (the
+  // only one in flight), then, once the first S / dP MFMAs are issued, start
+  // the DMA of tile kt+2 into the buffer tile kt-1 left (every wavefront
+  // passed the previous barrier after reading it) and convert this
+  // wavefront's part of tile kt+1; compute tile kt; publish.
   auto step = [&](int kt, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    if (kt + C::NS - 1 < nkt) issue(kt + C::NS - 1, (buf + C::NS - 1) % C::NS);
+    wait_vmem();
+    auto between = [&] {
+      if (kt + 2 < nkt) issue(kt + 2, (buf + 2) % C::NS);
+      if constexpr (DsOf<E>::kConvert)
+        if (kt + 1 < nkt) dma_tile_to_f16<HS, C::BN, C::NW>(Ks[(buf + 1) % C::NS], w, lane);
+    };
     const int key0 = kt * C::BN;
     const uint32_t g0 = uint32_t(key0 / 8 + h), ub = uint32_t(bh), uq = uint32_t(qrow);
     if (q0 < T && key0 <= q0) {
       if (key0 == q0)
         dq_step<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
-                                      uq, g0, ub, dr);
+                                      negD, uq, g0, ub, dr, between);
       else if (key0 + 32 == q0)
         dq_step<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
-                                      uq, g0, ub, dr);
+                                      negD, uq, g0, ub, dr, between);
       else
         dq_step<E, HS, kFull, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
-                                    uq, g0, ub, dr);
+                                    negD, uq, g0, ub, dr, between);
+    } else {
+      between();
     }
-    wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
-    if constexpr (DsOf<E>::kConvert)
-      if (kt + 1 < nkt) dma_tile_to_f16<HS, C::BN, C::NW>(Ks[(buf + 1) % C::NS], w, lane);
     __syncthreads();
   };
   ring_loop<C::NS>(nkt, step);
