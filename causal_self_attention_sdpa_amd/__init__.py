@@ -32,6 +32,8 @@ from ._binding import (  # noqa: F401
     gattn_bwd_dropout,
     gattn_bwd_dkdv,
     gattn_bwd_dq,
+    gattn_bwd_noalloc,
+    gattn_bwd_noalloc_max_bytes,
     gattn_bwd_preprocess,
     gattn_bwd_strided,
     gattn_bwd_workspace_bytes,

@@ -43,6 +43,10 @@ def load_library():
     lib.gattn_bwd_workspace_bytes.restype = sz
     lib.gattn_bwd.argtypes = [vp] * 9 + [i, i, i, i, f, i, vp, sz, vp]
     lib.gattn_bwd.restype = i
+    lib.gattn_bwd_noalloc.argtypes = [vp] * 9 + [i, i, i, i, f, i, vp]
+    lib.gattn_bwd_noalloc.restype = i
+    lib.gattn_bwd_noalloc_max_bytes.argtypes = []
+    lib.gattn_bwd_noalloc_max_bytes.restype = sz
     lib.gattn_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, i, vp, sz, vp]
     lib.gattn_bwd_preprocess.restype = i
     lib.gattn_bwd_dq.argtypes = [vp] * 7 + [i, i, i, i, f, i, vp, sz, vp]
@@ -149,6 +153,23 @@ def gattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale: float, workspace, stream=N
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.gattn_bwd(*ptrs, lp, *outs, B, H, T, hs, float(scale), dt, ws, nbytes,
                          _stream(stream)), "gattn_bwd")
+
+
+def gattn_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, scale: float, stream=None) -> None:
+    """gattn_bwd with the library's static device scratch instead of a workspace."""
+    lib = load_library()
+    B, H, T, hs = _shape4(q)
+    dt = _dtype_code(q)
+    ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in
+            ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"))]
+    lp = _dev(lse, "lse", (B, H, T), _torch().float32)
+    outs = [_dev(x, n, q.shape, q.dtype) for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    _check(lib.gattn_bwd_noalloc(*ptrs, lp, *outs, B, H, T, hs, float(scale), dt,
+                                 _stream(stream)), "gattn_bwd_noalloc")
+
+
+def gattn_bwd_noalloc_max_bytes() -> int:
+    return int(load_library().gattn_bwd_noalloc_max_bytes())
 
 
 def gattn_bwd_preprocess(o, dO, lse, workspace, stream=None) -> None:

@@ -5,8 +5,17 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "gattn_internal.h"
+
+// Device scratch of gattn_bwd_noalloc: the backward's row terms (what the
+// caller's workspace holds for gattn_bwd), for callers that cannot allocate.
+// Each GPU the library runs on holds its own copy for the life of the
+// process.  In host code `scratch` is only a stand-in for the symbol: its
+// device address comes from hipGetSymbolAddress (scratch_address below).
+static constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -157,15 +166,43 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, const 
   return check_shape(B, H, T, hs, dtype);
 }
 
-int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
-              const float* lse, const void* dq, const void* dk, const void* dv, int B, int H,
-              int T, int hs, float scale, int dtype, const void* ws, size_t wsb) {
+// Pointers, scale and shape of a backward call (everything but the workspace).
+int check_bwd_io(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                 const float* lse, const void* dq, const void* dk, const void* dv, int B, int H,
+                 int T, int hs, float scale, int dtype) {
   if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(o) || !ptr_ok(dO) || !ptr_ok(lse) ||
       !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv))
     return GATTN_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return GATTN_ERR_INVALID_ARG;
-  if (int st = check_shape(B, H, T, hs, dtype)) return st;
+  return check_shape(B, H, T, hs, dtype);
+}
+
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+              const float* lse, const void* dq, const void* dk, const void* dv, int B, int H,
+              int T, int hs, float scale, int dtype, const void* ws, size_t wsb) {
+  if (int st = check_bwd_io(q, k, v, o, dO, lse, dq, dk, dv, B, H, T, hs, scale, dtype))
+    return st;
   return check_workspace(ws, wsb, B, H, T, hs, dtype);
+}
+
+// Device address of `scratch` on the current device, looked up with that
+// device current the first time the device is seen and kept per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return GATTN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GATTN_OK;
 }
 
 }  // namespace
@@ -318,6 +355,26 @@ int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
                        kNoDropout, stream))
     return st;
   return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, c, c, c, kNoDropout,
+                   stream);
+}
+
+size_t gattn_bwd_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int gattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv, int B, int H, int T, int hs,
+                      float scale, int dtype, hipStream_t stream) {
+  if (int st = check_bwd_io(q, k, v, o, dO, lse, dq, dk, dv, B, H, T, hs, scale, dtype))
+    return st;
+  if (gattn_bwd_workspace_bytes(B, H, T, hs, dtype) > kScratchBytes) return GATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (int st = scratch_address(&ws)) return st;
+  // The row terms need no clearing: the dQ pass (or, for float32, the row
+  // pass) overwrites every one the dK/dV pass reads.
+  const gattn::Layout c = gattn::contiguous_layout(H, T, hs);
+  if (int st = dq_impl(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, ws, c, c, c,
+                       kNoDropout, stream))
+    return st;
+  return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, ws, c, c, c, kNoDropout,
                    stream);
 }
 

@@ -176,6 +176,27 @@ int gattn_bwd(const void* q, const void* k, const void* v, const void* o, const 
               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Backward that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): as gattn_bwd, with the row terms kept in a static
+ * device array of the library (gattn_bwd_noalloc_max_bytes() bytes, 8 MiB, one
+ * copy per GPU, held until the process ends) instead of a caller workspace.
+ * Calls at most gattn_bwd_workspace_bytes() <= that size: B*H*T up to about
+ * one million rows (WORKSPACE otherwise, before any HIP call).  The first call
+ * on a device looks up the array's device address (hipGetSymbolAddress) with
+ * that device current; the stream must belong to the current device.  Every
+ * call on a GPU shares its array: calls that overlap on one GPU (different
+ * streams, or host threads without ordering) race and give wrong results;
+ * calls ordered on one stream do not.  Results equal gattn_bwd's bit for bit.
+ */
+int gattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv,
+                      int B, int H, int T, int hs, float scale, int dtype, hipStream_t stream);
+
+/* Bytes of the static device array gattn_bwd_noalloc uses. */
+size_t gattn_bwd_noalloc_max_bytes(void);
+
+/*
  * Backward on strided tensors: as gattn_bwd, with q, k, v addressed by
  * qkv_strides, o and dO by o_strides, and dq, dk, dv by grad_strides (same
  * convention and checks as gattn_fwd_strided; NULL = contiguous).  For a GPT

@@ -262,3 +262,20 @@ def test_header_is_plain_c_and_the_c_caller_links(tmp_path):
     spec.loader.exec_module(mod)
     exe = mod.build(out=str(tmp_path / "gattn_c_roundtrip"))
     assert os.access(exe, os.X_OK)
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """gattn_bwd_noalloc validates like gattn_bwd, and rejects a problem whose
+    row terms do not fit its static scratch, before touching the GPU."""
+    cap = ga.gattn_bwd_noalloc_max_bytes()
+    assert cap == 8 << 20
+    f = lib.gattn_bwd_noalloc
+    s = ctypes.c_float(0.125)
+    assert f(*([P] * 9), 1, 1, 1 << 21, 32, s, 1, None) == WORKSPACE  # 2^21 rows: 16 MiB
+    rows_max = cap // 8  # D and lse*log2(e), 4 bytes each per row
+    assert ga.gattn_bwd_workspace_bytes(1, 1, rows_max, 32, ga.BF16) <= cap
+    assert ga.gattn_bwd_workspace_bytes(1, 1, rows_max + 64, 32, ga.BF16) > cap
+    assert f(*([P] * 9), 1, 1, rows_max + 64, 32, s, 1, None) == WORKSPACE
+    assert f(None, *([P] * 8), 1, 1, 8, 64, s, 1, None) == INVALID
+    assert f(*([P] * 9), 1, 1, 8, 48, s, 1, None) == UNSUPPORTED
+    assert f(*([P] * 9), 1, 1, 8, 64, ctypes.c_float(-1.0), 1, None) == INVALID
