@@ -28,6 +28,11 @@ int check_shape(int B, int H, int T, int hs, int dtype) {
   if (B < 1 || H < 1 || T < 1 || hs < 1) return GATTN_ERR_INVALID_ARG;
   if (dtype != GATTN_F32 && dtype != GATTN_BF16 && dtype != GATTN_F16) return GATTN_ERR_INVALID_ARG;
   if (int64_t(B) * H * T * hs >= (int64_t(1) << 31)) return GATTN_ERR_INVALID_ARG;
+  // The 16-bit kernels address one (b, h) slice with 32-bit byte offsets and
+  // touch rows up to the next tile boundary past T (fewer than 256 rows
+  // further): those must still fit, as for the strided layouts (layout_of).
+  if (dtype != GATTN_F32 && (int64_t(T) + 256) * hs * 2 >= (int64_t(1) << 31))
+    return GATTN_ERR_INVALID_ARG;
   if (dtype != GATTN_F32 && hs != 32 && hs != 64) return GATTN_ERR_UNSUPPORTED;
   if (dtype == GATTN_F32 && hs > 128) return GATTN_ERR_UNSUPPORTED;
   return GATTN_OK;

@@ -53,7 +53,9 @@
  * Errors: every function returns a gattn_status.  All argument checks run
  * before any HIP call, so an invalid call enqueues nothing.  INVALID_ARG: a
  * required pointer is NULL or not 16-byte aligned, B, H or T < 1, hs < 1,
- * scale not finite or <= 0, B*H*T*hs >= 2^31, or dtype unknown.
+ * scale not finite or <= 0, B*H*T*hs >= 2^31, dtype unknown, or, for bf16
+ * and fp16, (T + 256) * hs * 2 >= 2^31 (one slice's rows, plus the tile
+ * boundary past T, addressed with 32-bit byte offsets).
  * UNSUPPORTED: bf16 or fp16 with hs not in {32, 64}, or f32 with hs > 128.
  * WORKSPACE: workspace NULL, not 256-byte aligned, or smaller than
  * gattn_bwd_workspace_bytes().

@@ -73,3 +73,48 @@ def dkdv_columns(q, k, v, dO, scale: float, j0: int, j1: int):
         dv[: hi - j0] += np.outer(pj, dO[i])
         dk[: hi - j0] += scale * np.outer(dS, q[i])
     return dk, dv
+
+
+def forward_all_rows(q, k, v, scale: float, block: int = 256):
+    """o and lse of every query row of one (T, hs) slice, the rows taken in
+    blocks of `block` so that each row's scores, mask, softmax and value sum
+    (the definitions above, one row at a time) run as matrix products."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    T, hs = q.shape
+    o = np.empty((T, hs))
+    lse = np.empty(T)
+    for r0 in range(0, T, block):
+        r1 = min(T, r0 + block)
+        s = q[r0:r1] @ k[:r1].T
+        s *= scale
+        # keys after row i lie in the block's own columns r0 .. r1-1 only
+        diag = s[:, r0:r1]
+        diag[np.triu(np.ones((r1 - r0, r1 - r0), dtype=bool), 1)] = -np.inf
+        m = s.max(axis=1, keepdims=True)
+        s -= m
+        np.exp(s, out=s)
+        l = s.sum(axis=1, keepdims=True)
+        o[r0:r1] = (s @ v[:r1]) / l
+        lse[r0:r1] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def dkdv_block(q, k, v, dO, scale: float, j0: int, j1: int, o, lse, block: int = 256):
+    """dk and dv of keys j0 .. j1-1 from every row i >= j0, given the rows' o
+    and lse (from forward_all_rows): P[i][j] = exp(s[i][j] - lse[i]) and
+    D[i] = dO[i] . o[i] as in the header; rows taken in blocks."""
+    q, k, v, dO, o, lse = (np.asarray(a, dtype=np.float64) for a in (q, k, v, dO, o, lse))
+    T, hs = q.shape
+    dk = np.zeros((j1 - j0, hs))
+    dv = np.zeros((j1 - j0, hs))
+    kj, vj = k[j0:j1], v[j0:j1]
+    for r0 in range(j0, T, block):
+        r1 = min(T, r0 + block)
+        s = (q[r0:r1] @ kj.T) * scale
+        p = np.exp(s - lse[r0:r1, None])
+        p[np.arange(j0, j1)[None, :] > np.arange(r0, r1)[:, None]] = 0.0
+        D = np.sum(dO[r0:r1] * o[r0:r1], axis=1)
+        dS = p * (dO[r0:r1] @ vj.T - D[:, None])
+        dv += p.T @ dO[r0:r1]
+        dk += scale * (dS.T @ q[r0:r1])
+    return dk, dv

@@ -279,3 +279,18 @@ def test_noalloc_rejects_before_any_hip_call(lib):
     assert f(None, *([P] * 8), 1, 1, 8, 64, s, 1, None) == INVALID
     assert f(*([P] * 9), 1, 1, 8, 48, s, 1, None) == UNSUPPORTED
     assert f(*([P] * 9), 1, 1, 8, 64, ctypes.c_float(-1.0), 1, None) == INVALID
+
+
+def test_contiguous_16bit_slice_byte_limit(lib):
+    """A bf16/fp16 slice whose T + 256 rows reach 2^31 bytes is rejected on the
+    contiguous path as on the strided one (the kernels address a slice with
+    32-bit byte offsets); B*H*T*hs alone stays below 2^31 there."""
+    limit = (1 << 24) - 256  # (limit + 256) * 64 * 2 == 2^31
+    assert (limit + 256) * 64 * 2 == 1 << 31 and limit * 64 < 1 << 31
+    for dt in (ga.BF16, ga.F16):
+        assert ga.gattn_bwd_workspace_bytes(1, 1, limit, 64, dt) == 0
+        assert ga.gattn_bwd_workspace_bytes(1, 1, limit - 1, 64, dt) > 0
+        assert _fwd(lib, T=limit, hs=64, dtype=dt) == INVALID
+        assert _fwd(lib, T=2 * limit + 256, hs=32, dtype=dt) == INVALID
+    # float32 addresses rows with 64-bit offsets: only B*H*T*hs < 2^31 applies
+    assert ga.gattn_bwd_workspace_bytes(1, 1, limit, 64, ga.F32) > 0

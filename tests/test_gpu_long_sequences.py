@@ -8,15 +8,19 @@ oracle's single-row functions (oracle.rows, pinned against the whole-problem
 oracle) check what is cheap to compute exactly:
   * o and lse of query rows at the start, the middle and the end;
   * dq of the same rows (a row's dq needs only that row);
-  * dk and dv of a block of keys (all of them for T = 8192 from the middle of
-    the sequence, the last tile's keys for the longer lengths: a key's
-    gradients need every row after it);
+  * dk and dv of a block of keys: from the middle for T = 8192, the last
+    tile's keys for the longer lengths (a key's gradients need every row
+    after it), and at T = 32768 and 65536 also keys 0 .. 127, whose dK/dV
+    workgroup walks every query tile of the sequence (the longest loop), from
+    the row-blocked oracle (every row's o and lse in float64, then the key
+    block's gradients from all rows);
 all to the bf16 bar 2e-2 + 2^-8 |ref| (float32: 1e-4) on unit-variance
-inputs; and on the whole output two identities that hold at any size
-because each softmax row sums to one: the keys' dv sum to the queries' dO,
-and the keys' dk sum to zero (every row of dS = P (dP - D) sums to zero),
-per (b, h) and column, to within 2^-6 of the summed terms' absolute mass
-(a tile lost or counted twice moves these sums by a large part of it).
+inputs.  Two identities that hold at any size because each softmax row sums
+to one are checked on the whole output as a coarse sanity bound: the keys' dv
+sum to the queries' dO and the keys' dk sum to zero, per (b, h) and column,
+to within 2^-6 of the summed terms' absolute mass.  (They cannot see a lost
+tile at these lengths: a tile's weights are of order 1/T; the key blocks at
+both ends of the sequence are the checks for that.)
 """
 import numpy as np
 import pytest
@@ -44,9 +48,11 @@ def _close(got, ref, tol, rel, what):
                            f"got {got[tuple(bad[0])]}, ref {ref[tuple(bad[0])]}")
 
 
-@pytest.mark.parametrize("dtype,T,kblock", [("bf16", 8192, (4096, 4160)), ("bf16", 32768, None),
-                                            ("bf16", 65536, None), ("f32", 8192, None)])
-def test_long_sequence_rows_columns_and_sum_rules(dtype, T, kblock):
+@pytest.mark.parametrize("dtype,T,kblock,start", [("bf16", 8192, (4096, 4160), False),
+                                                  ("bf16", 32768, None, True),
+                                                  ("bf16", 65536, None, True),
+                                                  ("f32", 8192, None, False)])
+def test_long_sequence_rows_columns_and_sum_rules(dtype, T, kblock, start):
     import causal_self_attention_sdpa_amd as ga
     from oracle import rows
     B, H, hs = 1, 2, 64
@@ -79,3 +85,11 @@ def test_long_sequence_rows_columns_and_sum_rules(dtype, T, kblock):
         assert np.all(np.abs(gdv.sum(0) - dO.sum(0))
                       <= 2.0 ** -6 * (np.abs(gdv).sum(0) + np.abs(dO).sum(0))), f"sum dv h={h}"
         assert np.all(np.abs(gdk.sum(0)) <= 2.0 ** -6 * np.abs(gdk).sum(0)), f"sum dk h={h}"
+    if start:
+        # Keys 0 .. 127 of head 0: the dK/dV workgroup that walks all T/64 query tiles.
+        q, k, v, dO = (x[n][0, 0] for n in ("q", "k", "v", "do"))
+        print(f"  key block 0..127 of T={T}: row-blocked oracle", flush=True)
+        fo, fl = rows.forward_all_rows(q, k, v, s)
+        bdk, bdv = rows.dkdv_block(q, k, v, dO, s, 0, 128, fo, fl)
+        _close(got["dk"][0, 0, :128], bdk, tol, rel, f"dk keys 0..127 T={T}")
+        _close(got["dv"][0, 0, :128], bdv, tol, rel, f"dv keys 0..127 T={T}")

@@ -303,3 +303,23 @@ def test_rows_and_columns_equal_the_whole_problem_oracle(T, hs, scale):
     mdk, mdv = rows.dkdv_columns(q, k, v, dO, scale, j0, j1)
     np.testing.assert_allclose(mdk, dk[0, 0, j0:j1], rtol=0, atol=1e-12)
     np.testing.assert_allclose(mdv, dv[0, 0, j0:j1], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,hs,scale,block", [(37, 16, 0.3, 8), (200, 8, 1.1, 64), (64, 4, 0.5, 100)])
+def test_blocked_rows_equal_the_whole_problem_oracle(T, hs, scale, block):
+    """oracle.rows.forward_all_rows / dkdv_block batch independent rows into
+    blocks of matrix products (blocks smaller than, straddling and larger than
+    T); every row's o and lse and a key range's dk and dv (from the start, the
+    middle and the end, given those rows) equal the C++ oracle to float64
+    rounding."""
+    from oracle import rows
+    q, k, v, dO = (_rand((T, hs), 70 + i) for i in range(4))
+    dq, dk, dv, o, lse = oracle.attention_backward(q[None, None], k[None, None], v[None, None],
+                                                   dO[None, None], scale)
+    bo, bl = rows.forward_all_rows(q, k, v, scale, block=block)
+    np.testing.assert_allclose(bo, o[0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(bl, lse[0, 0], rtol=0, atol=1e-12)
+    for j0, j1 in ((0, min(T, 13)), (T // 2, T // 2 + 5), (T - 3, T)):
+        bdk, bdv = rows.dkdv_block(q, k, v, dO, scale, j0, j1, bo, bl, block=block)
+        np.testing.assert_allclose(bdk, dk[0, 0, j0:j1], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(bdv, dv[0, 0, j0:j1], rtol=0, atol=1e-12)
