@@ -17,11 +17,12 @@
 //                                   whole loop (B operand), K rows read from
 //                                   LDS in perm_row order so each lane's
 //                                   registers 8t..8t+7 are 8 consecutive keys;
-//   online softmax in base 2 (running max m and sum l per query = per lane,
-//   so the rescale factor is a per-lane scalar).  A row's reference max m
-//   only moves when the row's maximum exceeds it by more than 2^8 in the
-//   base-2 domain, so the weights stay <= 256 (well inside the 16-bit and float32 ranges)
-//   and the output is rescaled only on those rare tiles;
+//   online softmax in base 2 (reference max m and sum l per query = per
+//   lane, so the rescale factor is a per-lane scalar).  A row's reference
+//   max m only moves when its weights against the current m would grow past
+//   2^8 (the test uses the weights' sums, so the common tile needs no row
+//   max), so the weights stay <= 256 (well inside the 16-bit and float32
+//   ranges) and the output is rescaled only on those rare halves;
 //   O^T (hs x queries) += V^T P^T  on MFMA, P^T straight from the S^T
 //                                   accumulators (no LDS round trip), V^T
 //                                   read from the row-major V tile with LDS
@@ -79,16 +80,49 @@ struct FwdState {
 //            the diagonal block.
 enum TileKind { kFull = 0, kDiagLo = 1, kDiagHi = 2 };
 
+// The weights of one 32-key half (registers s of a score block) against the
+// reference max m (mc = m * c): P^T operand pairs in pf and, returned, the
+// lane's sum of its 16 weights before dropout.  bits: the two 8-key runs'
+// keep bits (DROP).
+template <class E, bool DROP>
+__device__ __forceinline__ float half_weights(const f32x16& s, float c, float mc,
+                                              const uint32_t (&bits)[2], u32x4 (&pf)[2]) {
+  float ls;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * t + 2 * e], c, -mc));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * t + 2 * e + 1], c, -mc));
+      if constexpr (DROP)
+        pf[t][e] = E::pack(keep_or_zero(p0, bits[t], 2 * e), keep_or_zero(p1, bits[t], 2 * e + 1));
+      else
+        pf[t][e] = E::pack(p0, p1);
+      ls = t == 0 && e == 0 ? p0 + p1 : ls + (p0 + p1);
+    }
+  return ls;
+}
+
 // One key tile for one wavefront.  `dn` = n - 8h: in the diagonal block,
 // register i of lane (n, h) holds key (q0 + 16*(i/8) + 8h + i%8), which lies
 // above query q0 + n exactly when 16*(i/8) + i%8 > dn.  With DROP, the run of
 // registers 8t..8t+7 of half kh is keys 8 * (g0 + 4 kh + 2 t) .. +7 of query
 // qrow (g0 = key0 / 8 + h).
+//
+// The tile's weights are first formed against the row's current reference
+// max m; only a row whose weights in one of its two lanes sum past 2^8, or
+// are not finite (the row's first tile, where m = -inf, or a NaN or infinite
+// score), moves m to its running maximum, rescales l and O and forms the
+// tile's weights again.
+// So every weight that reaches the MFMA or l is <= 2^8 (well inside the 16-bit
+// and float32 ranges), the row max is computed only on those rare tiles, and
+// the decision is per row: a row's result never depends on other rows.
 template <class E, int HS, int KIND, bool DROP>
-__device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb, int dn, float c,
-                                         const LaneOffsets<HS>& L, const u32x4 (&qf)[HS / 16],
-                                         FwdState<HS>& st, uint32_t qrow, uint32_t g0,
-                                         uint32_t bh, const Dropout& dr) {
+__device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb, int n, int dn,
+                                         float c, const LaneOffsets<HS>& L,
+                                         const u32x4 (&qf)[HS / 16], FwdState<HS>& st,
+                                         uint32_t qrow, uint32_t g0, uint32_t bh,
+                                         const Dropout& dr) {
   using C = FwdCfg<HS>;
   constexpr int NKH = KIND == kDiagLo ? 1 : 2;  // 32-key halves computed
   f32x16 s[2];
@@ -106,46 +140,35 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb,
     for (int i = 0; i < 16; ++i)
       if (16 * (i >> 3) + (i & 7) > dn) s[kd][i] = -INFINITY;
   }
-  // Row max: one max3 chain per half.
-  float mh[NKH];
+  uint32_t bits[2][2] = {{0xFFu, 0xFFu}, {0xFFu, 0xFFu}};
+  if constexpr (DROP)
 #pragma unroll
-  for (int kh = 0; kh < NKH; ++kh) {
-    mh[kh] = fmaxf(s[kh][0], s[kh][1]);
+    for (int kh = 0; kh < NKH; ++kh)
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) mh[kh] = fmaxf(fmaxf(mh[kh], s[kh][i]), s[kh][i + 1]);
-  }
-  const float mt = halves_max(NKH == 2 ? fmaxf(mh[0], mh[1]) : mh[0]);
-  // Each row moves its reference max only if its weights would exceed 2^8
-  // (a per-row decision, so a row's result never depends on other rows).
-  // The multiply is skipped when no row of the wavefront moved; rows that
-  // keep their max are multiplied by exactly 1.
-  const float mn = (mt - st.m) * c > 8.f ? fmaxf(st.m, mt) : st.m;
-  if (__builtin_amdgcn_ballot_w64(mn != st.m)) {
-    const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);  // m = -inf first: alpha = 0
+      for (int t = 0; t < 2; ++t) bits[kh][t] = keep_bits8(qrow, g0 + 4 * kh + 2 * t, bh, dr);
+  u32x4 pf[2][2];
+  float ls = half_weights<E, DROP>(s[0], c, st.m * c, bits[0], pf[0]);
+  if constexpr (NKH == 2) ls += half_weights<E, DROP>(s[1], c, st.m * c, bits[1], pf[1]);
+  const uint64_t over = __builtin_amdgcn_ballot_w64(!(ls <= 256.f));
+  if (over) {
+    const uint32_t rows = uint32_t(over) | uint32_t(over >> 32);
+    float mh = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int kh = 0; kh < NKH; ++kh)
+#pragma unroll
+      for (int i = kh == 0 ? 2 : 0; i < 16; i += 2) mh = fmaxf(fmaxf(mh, s[kh][i]), s[kh][i + 1]);
+    mh = halves_max(mh);
+    // Rows that keep m are multiplied by exactly 1; m = -inf gives alpha = 0.
+    const float mn = (rows >> n) & 1u ? fmaxf(st.m, mh) : st.m;
+    const float alpha = __builtin_amdgcn_exp2f((st.m - mn) * c);
     st.l *= alpha;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) st.oacc[db] *= alpha;
     st.m = mn;
+    ls = half_weights<E, DROP>(s[0], c, st.m * c, bits[0], pf[0]);
+    if constexpr (NKH == 2) ls += half_weights<E, DROP>(s[1], c, st.m * c, bits[1], pf[1]);
   }
-  const float mc = st.m * c;
-  u32x4 pf[2][2];
-#pragma unroll
-  for (int kh = 0; kh < NKH; ++kh)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint32_t bits = 0xFFu;
-      if constexpr (DROP) bits = keep_bits8(qrow, g0 + 4 * kh + 2 * t, bh, dr);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e], c, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kh][8 * t + 2 * e + 1], c, -mc));
-        if constexpr (DROP)
-          pf[kh][t][e] = E::pack(keep_or_zero(p0, bits, 2 * e), keep_or_zero(p1, bits, 2 * e + 1));
-        else
-          pf[kh][t][e] = E::pack(p0, p1);
-        st.l += p0 + p1;
-      }
-    }
+  st.l += ls;
 #pragma unroll
   for (int kh = 0; kh < NKH; ++kh)
 #pragma unroll
@@ -220,11 +243,11 @@ __global__ __launch_bounds__(kThreads) void fwd16_kernel(const uint16_t* __restr
     const uint32_t g0 = uint32_t(key0 / 8 + h);
     if (q0 < T && key0 <= q0) {  // this wavefront sees some key of the tile
       if (key0 == q0)
-        fwd_tile<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], dn, c, L, qf, st, qrow, g0, bh, dr);
+        fwd_tile<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], n, dn, c, L, qf, st, qrow, g0, bh, dr);
       else if (key0 + 32 == q0)
-        fwd_tile<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], dn, c, L, qf, st, qrow, g0, bh, dr);
+        fwd_tile<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], n, dn, c, L, qf, st, qrow, g0, bh, dr);
       else
-        fwd_tile<E, HS, kFull, DROP>(Ks[buf], Vs[buf], dn, c, L, qf, st, qrow, g0, bh, dr);
+        fwd_tile<E, HS, kFull, DROP>(Ks[buf], Vs[buf], n, dn, c, L, qf, st, qrow, g0, bh, dr);
     }
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
