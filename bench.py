@@ -482,11 +482,12 @@ def main() -> int:
         for g in ("dq", "dk", "dv"):
             t[g] = torch.empty_like(t["q"])
         layers.append(t)
-    ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, dcode), dtype=torch.uint8,
-                     device=dev)
+    drop = args.dropout > 0.0
+    wsn = (ga.gattn_bwd_dropout_workspace_bytes(B, H, T, hs, dcode, args.dropout) if drop
+           else ga.gattn_bwd_workspace_bytes(B, H, T, hs, dcode))
+    ws = torch.empty(wsn, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     timer = HipTimer()
-    drop = args.dropout > 0.0
     if drop and args.layout != "contiguous":
         print("--dropout is measured with the contiguous layout only", file=sys.stderr)
         return 2

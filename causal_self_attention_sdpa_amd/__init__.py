@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     attention_forward_qkv,
     gattn_bwd,
     gattn_bwd_dropout,
+    gattn_bwd_dropout_workspace_bytes,
     gattn_bwd_dkdv,
     gattn_bwd_dq,
     gattn_bwd_noalloc,

@@ -67,6 +67,8 @@ def load_library():
     lib.gattn_bwd_dropout.argtypes = ([vp] * 9 + [i, i, i, i, f, i, f, u64, u32, vp, sz]
                                       + [vp, vp, vp, vp])
     lib.gattn_bwd_dropout.restype = i
+    lib.gattn_bwd_dropout_workspace_bytes.argtypes = [i, i, i, i, i, f]
+    lib.gattn_bwd_dropout_workspace_bytes.restype = sz
     lib.gattn_dropout_mask.argtypes = [vp, i, i, i, f, u64, u32, vp]
     lib.gattn_dropout_mask.restype = i
     lib.gattn_probe_mfma_bf16.argtypes = [vp, i, i, vp]
@@ -317,6 +319,11 @@ def gattn_fwd_dropout(q, k, v, o, lse, scale: float, p: float, seed: int, offset
                                  _stream(stream)), "gattn_fwd_dropout")
 
 
+def gattn_bwd_dropout_workspace_bytes(B: int, H: int, T: int, hs: int, dtype: int,
+                                      p: float) -> int:
+    return int(load_library().gattn_bwd_dropout_workspace_bytes(B, H, T, hs, dtype, float(p)))
+
+
 def gattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, scale: float, p: float, seed: int,
                       offset: int, workspace, stream=None) -> None:
     """Backward of gattn_fwd_dropout (same p, seed, offset); strided views as
@@ -365,7 +372,7 @@ def attention_backward_dropout(q, k, v, o, dO, lse, p: float, seed: int, offset:
     torch = _torch()
     B, H, T, hs = _shape4(q)
     if workspace is None:
-        n = gattn_bwd_workspace_bytes(B, H, T, hs, _dtype_code(q))
+        n = gattn_bwd_dropout_workspace_bytes(B, H, T, hs, _dtype_code(q), p)
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     gattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, _default_scale(hs, scale), p, seed,

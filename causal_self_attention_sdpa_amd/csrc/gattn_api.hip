@@ -125,6 +125,11 @@ int pre_impl(const void* o, const void* dO, const float* lse, int B, int H, int 
                                       hs, lo, dtype == GATTN_F16, stream));
 }
 
+// Keep-bit blocks of the 16-bit backward with dropout, after D and L2.
+uint64_t* ws_keep(void* ws, int B, int H, int T) {
+  return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + 2 * ws_part_bytes(B, H, T));
+}
+
 int dq_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
             const float* lse, void* dq, int B, int H, int T, int hs, float scale, int dtype,
             void* workspace, gattn::Layout li, gattn::Layout lo, gattn::Layout lg,
@@ -141,8 +146,9 @@ int dq_impl(const void* q, const void* k, const void* v, const void* o, const vo
   return status_of(gattn::h16_bwd_dq(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
-      static_cast<const uint16_t*>(dO), lse, D, L2, static_cast<uint16_t*>(dq), B * H, H, T, hs,
-      scale, li, lo, lg, dr, dtype == GATTN_F16, stream));
+      static_cast<const uint16_t*>(dO), lse, D, L2,
+      dr.thr != 0 ? ws_keep(workspace, B, H, T) : nullptr, static_cast<uint16_t*>(dq), B * H, H,
+      T, hs, scale, li, lo, lg, dr, dtype == GATTN_F16, stream));
 }
 
 int dkdv_impl(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
@@ -159,8 +165,9 @@ int dkdv_impl(const void* q, const void* k, const void* v, const void* dO, void*
   return status_of(gattn::h16_bwd_dkdv(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), D, L2,
-      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B * H, H, T, hs, scale, li, lo, lg,
-      dr, dtype == GATTN_F16, stream));
+      dr.thr != 0 ? ws_keep(workspace, B, H, T) : nullptr, static_cast<uint16_t*>(dk),
+      static_cast<uint16_t*>(dv), B * H, H, T, hs, scale, li, lo, lg, dr, dtype == GATTN_F16,
+      stream));
 }
 
 int check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -228,6 +235,15 @@ const char* gattn_status_string(int status) {
 size_t gattn_bwd_workspace_bytes(int B, int H, int T, int hs, int dtype) {
   if (check_shape(B, H, T, hs, dtype) != GATTN_OK) return 0;
   return 2 * ws_part_bytes(B, H, T);
+}
+
+size_t gattn_bwd_dropout_workspace_bytes(int B, int H, int T, int hs, int dtype, float p) {
+  gattn::Dropout dr;
+  if (check_shape(B, H, T, hs, dtype) != GATTN_OK || dropout_of(p, 0, 0, dr) != GATTN_OK) return 0;
+  const size_t base = 2 * ws_part_bytes(B, H, T);
+  if (dtype == GATTN_F32 || dr.thr == 0) return base;
+  if ((int64_t(T) + 7) / 8 > gattn::kKeepMaxGroups) return 0;
+  return base + gattn::ws_keep_bytes(B, H, T);
 }
 
 int gattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -413,6 +429,10 @@ int gattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o
     return st;
   gattn::Dropout dr;
   if (int st = dropout_of(p, seed, offset, dr)) return st;
+  if (dtype != GATTN_F32 && dr.thr != 0 && (int64_t(T) + 7) / 8 > gattn::kKeepMaxGroups)
+    return GATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < gattn_bwd_dropout_workspace_bytes(B, H, T, hs, dtype, p))
+    return GATTN_ERR_WORKSPACE;
   gattn::Layout li, lo, lg;
   if (int st = layout_of(qkv_strides, H, T, hs, dtype, li)) return st;
   if (int st = layout_of(o_strides, H, T, hs, dtype, lo)) return st;

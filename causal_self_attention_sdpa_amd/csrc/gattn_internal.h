@@ -134,6 +134,16 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline size_t ws_part_bytes(int B, int H, int T) {
   return align256(sizeof(float) * size_t(B) * H * T);
 }
+// Keep-bit blocks of the 16-bit backward with dropout: per (b, h) slice,
+// ng x ng blocks of 8 bytes (ng = ceil(T / 8); block (query octet, key
+// group), byte e = query 8 * octet + e, bit r = key 8 * group + r).  The
+// kernels address one slice's blocks with 32-bit offsets: kKeepMaxGroups
+// bounds ng.
+constexpr int64_t kKeepMaxGroups = 16383;
+inline size_t ws_keep_bytes(int B, int H, int T) {
+  const size_t ng = (size_t(T) + 7) / 8;
+  return align256(size_t(B) * H * ng * ng * 8);
+}
 
 // ---- float32 path (any hs <= 128, any T; wave per row; deterministic) ----
 // li: layout of q, k, v; lo: of o, dO; lg: of dq, dk, dv.  lse, D and L2 are
@@ -173,14 +183,17 @@ hipError_t dropout_mask(uint8_t* keep, int BH, int T, const Dropout& dr, hipStre
 hipError_t h16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
                        float* L2, int BH, int H, int T, int hs, Layout lo, bool f16,
                        hipStream_t s);
+// keep: with dropout (dr.thr != 0) the keep-bit blocks, ws_keep_bytes(BH, T)
+// bytes: written by h16_bwd_dq, read by h16_bwd_dkdv; unused otherwise.
 hipError_t h16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
-                        uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
-                        Layout lo, Layout lg, const Dropout& dr, bool f16, hipStream_t s);
+                        const uint16_t* dO, const float* D, const float* L2,
+                        const uint64_t* keep, uint16_t* dk, uint16_t* dv, int BH, int H, int T,
+                        int hs, float scale, Layout li, Layout lo, Layout lg, const Dropout& dr,
+                        bool f16, hipStream_t s);
 hipError_t h16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                      float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
-                      Layout li, Layout lo, Layout lg, const Dropout& dr, bool f16,
+                      float* L2, uint64_t* keep, uint16_t* dq, int BH, int H, int T, int hs,
+                      float scale, Layout li, Layout lo, Layout lg, const Dropout& dr, bool f16,
                       hipStream_t s);
 
 }  // namespace gattn

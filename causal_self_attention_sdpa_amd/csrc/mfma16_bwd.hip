@@ -109,13 +109,15 @@ __global__ __launch_bounds__(kThreads) void pre16_kernel(const uint16_t* __restr
 // In the steps that meet the diagonal, blocks wholly before this wavefront's
 // keys are skipped and the others masked.
 //
-// Dropout here sees a weight's keep decision in the transposed position: a
-// lane holds 8 consecutive queries of one key, while a generator block
-// covers 8 consecutive keys of one query.  The 8 lanes n = 8a .. 8a+7 (same
-// h) hold keys 8G .. 8G+7 against the same 8 queries I0 .. I0+7, so lane
-// 8a + r draws the block of query I0 + r, and the 8 blocks' keep bytes are
-// exchanged among the 8 lanes (xor 1, 2, 4); the lane then reads bit r of
-// byte e for query I0 + e.
+// With dropout the keep decisions are not drawn here: the dQ kernel, which
+// runs first and draws every decision of the causal pairs (one generator
+// block = 8 consecutive keys of one query), stores them in the workspace as
+// 8x8 blocks: block (query octet I, key group G) is 8 bytes at
+// ((I * ng + G) * 8) of the slice's part (ng = ceil(T / 8)), byte e holding
+// query 8I + e's bits, bit r key 8G + r.  Each step DMAs the 8 x 16 blocks of
+// its 64 queries and the workgroup's 128 keys into LDS next to the Q and dO
+// tiles; a lane (8 consecutive queries of one key per run) reads one block
+// per run and bit r of byte e.
 template <int HS>
 struct DkdvCfg {
   static constexpr int NW = 4;
@@ -126,20 +128,29 @@ struct DkdvCfg {
   static constexpr int DB = HS / 32;
   static constexpr int NS = GATTN_DKDV_STAGES;  // LDS ring depth
   // DMA instructions per wavefront per step: Q and dO tiles, plus one quarter
-  // of the lse and D rows each.
+  // of the lse and D rows each (with dropout, one more: a quarter of the
+  // step's keep-bit blocks).
   static constexpr int PER = 2 * (BQ * HS / 512) / NW + 2;
+  static constexpr int KEEP_WORDS = (BQ / 8) * (BN / 8) * 2;  // keep-bit tile, 32-bit words
   static_assert((BQ * HS / 512) % NW == 0 && BQ % (4 * NW) == 0, "uniform DMA split");
 };
 
+// kf, vf: the lane's K and V fragments (B operands of A(b)), held in
+// registers in the contiguous kernel without dropout; with dropout or
+// strided layouts they are read from the workgroup's K and V tiles in LDS
+// for each block instead (KVb: K tile, then V tile), which leaves the
+// registers the masks or the strides need.
 template <int HS>
 struct DkdvRegs {
   u32x4 kf[HS / 16], vf[HS / 16];
   f32x16 dka[HS / 32], dva[HS / 32];
 };
 
-// A(b): S and dP of query block qb.
-template <class E, int HS>
-__device__ __forceinline__ void dkdv_sdp(const uint16_t* Qb, const uint16_t* Gb, int qb,
+// A(b): S and dP of query block qb.  kl: the lane's key row in the
+// workgroup's tiles.
+template <class E, int HS, bool KVL>
+__device__ __forceinline__ void dkdv_sdp(const uint16_t* Qb, const uint16_t* Gb,
+                                const uint16_t* KVb, int kl, int h, int qb,
                                 const LaneOffsets<HS>& L, const DkdvRegs<HS>& R, f32x16& s,
                                 f32x16& dp) {
   using C = DkdvCfg<HS>;
@@ -147,58 +158,38 @@ __device__ __forceinline__ void dkdv_sdp(const uint16_t* Qb, const uint16_t* Gb,
   dp = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < C::KSTEP; ++ks) {
-    s = DsOf<E>::T::mfma(op_nat<HS>(Qb, L, qb * 32, ks), R.kf[ks], s);
-    dp = E::mfma(op_nat<HS>(Gb, L, qb * 32, ks), R.vf[ks], dp);
+    const u32x4 kf = KVL ? tile_row16<HS>(KVb, kl, 16 * ks + 8 * h) : R.kf[ks];
+    const u32x4 vf = KVL ? tile_row16<HS>(KVb + C::BN * HS, kl, 16 * ks + 8 * h) : R.vf[ks];
+    s = DsOf<E>::T::mfma(op_nat<HS>(Qb, L, qb * 32, ks), kf, s);
+    dp = E::mfma(op_nat<HS>(Gb, L, qb * 32, ks), vf, dp);
   }
 }
 
-// Lane xor M within each group of 32 lanes (ds_swizzle, bit-mask mode).
-template <int M>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
-  return uint32_t(__builtin_amdgcn_ds_swizzle(int(x), (M << 10) | 0x1F));
+// Keep bits of this lane's run t of 8 queries in query block qb (queries
+// qs0 + 32 qb + 16 t + 8h + e) for its key, from the step's keep-bit tile Bb
+// (block of query octet a, key group gl at words 2 (16 a + gl) and +1);
+// r = key & 7.  Bit 8e of w[0] (e < 4) or of w[1] (e >= 4) is then the
+// decision for query e of the run.
+__device__ __forceinline__ u32x2 dkdv_keep(const uint32_t* Bb, int qb, int t, int h, int gl,
+                                           int r) {
+  const u32x2 blk = *reinterpret_cast<const u32x2*>(Bb + 2 * (16 * (4 * qb + 2 * t + h) + gl));
+  return u32x2{blk[0] >> r, blk[1] >> r};
 }
 
-// The keep bytes of the 8 lanes 8a .. 8a+7 (lane 8a + r passes `byte`, r =
-// lane & 7): byte e of (lo, hi) as one 64-bit word is lane 8a + e's byte.
-// Placement by per-lane shifts and a bit-field insert (no compares).
-__device__ __forceinline__ void gather8(uint32_t byte, int r, uint32_t& lo, uint32_t& hi) {
-  const uint32_t s1 = 8u * (r & 1), s2 = 8u * (r & 2);  // 0 or 8; 0 or 16
-  const uint32_t m4 = 0u - uint32_t((r >> 2) & 1);      // all ones for the upper 4 lanes
-  const uint32_t p1 = xor_lane<1>(byte);
-  const uint32_t x16 = (byte << s1) | (p1 << (8u - s1));
-  const uint32_t p2 = xor_lane<2>(x16);
-  const uint32_t x32 = (x16 << s2) | (p2 << (16u - s2));
-  const uint32_t p4 = xor_lane<4>(x32);
-  lo = (p4 & m4) | (x32 & ~m4);
-  hi = (x32 & m4) | (p4 & ~m4);
-}
-
-// Keep bits of this lane's two runs of 8 queries in query block qb (run t:
-// queries qs0 + 32 qb + 16 t + 8h + e): bit 8e of w[t][0] (e < 4) or of
-// w[t][1] (e >= 4) is the decision for query e of the run and key krow.
-__device__ __forceinline__ void dkdv_keep(int qs0, int qb, int krow, int h, uint32_t bh,
-                                          const Dropout& dr, uint32_t (&w)[2][2]) {
-  const int r = krow & 7;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int q = qs0 + qb * 32 + 16 * t + 8 * h + r;
-    gather8(keep_bits8(uint32_t(q), uint32_t(krow) >> 3, bh, dr), r, w[t][0], w[t][1]);
-    w[t][0] >>= r;
-    w[t][1] >>= r;
-  }
-}
-
-// B(b) then C(b) for query block qb; w: its keep bits (DROP).
+// B(b) then C(b) for query block qb; with DROP, the keep bits come from the
+// step's keep-bit tile Bb (this lane's key group gl), read run by run.
 template <class E, int HS, bool MASK, bool DROP>
 __device__ __forceinline__ void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
-                                 const float* Db, int qb, int qs0, int krow, int h, float c,
-                                 const LaneOffsets<HS>& L, const f32x16& s, const f32x16& dp,
-                                 DkdvRegs<HS>& R, const uint32_t (&w)[2][2], float zs) {
+                                 const float* Db, const uint32_t* Bb, int qb, int qs0, int krow,
+                                 int h, float c, const LaneOffsets<HS>& L, const f32x16& s,
+                                 const f32x16& dp, DkdvRegs<HS>& R, int gl, float zs) {
   using C = DkdvCfg<HS>;
   u32x4 pp[2], dsp[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int ql = qb * 32 + 16 * t + 8 * h;  // local index of this lane's run of 8 queries
+    u32x2 w = {};
+    if constexpr (DROP) w = dkdv_keep(Bb, qb, t, h, gl, krow & 7);
     const f32x4 l0 = *reinterpret_cast<const f32x4*>(Lb + ql);
     const f32x4 l1 = *reinterpret_cast<const f32x4*>(Lb + ql + 4);
     const f32x4 d0 = *reinterpret_cast<const f32x4*>(Db + ql);
@@ -211,7 +202,7 @@ __device__ __forceinline__ void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb
       float p = __builtin_amdgcn_exp2f(fmaf(s[8 * t + e], c, -le));
       if (MASK && krow > qs0 + ql + e) p = 0.f;
       if constexpr (DROP) {
-        const uint32_t m = keep_mask(w[t][e >> 2], 8 * (e & 3));
+        const uint32_t m = keep_mask(w[e >> 2], 8 * (e & 3));
         pv[e] = __uint_as_float(__float_as_uint(p) & m);
         dsv[e] = p * (__uint_as_float(__float_as_uint(dp[8 * t + e] * zs) & m) - De);
       } else {
@@ -235,51 +226,39 @@ __device__ __forceinline__ void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb
     }
 }
 
-// One step below the diagonal: every block is visible, no mask.
-template <class E, int HS, bool DROP>
+// One step below the diagonal: every block is visible, no mask.  S and dP of
+// both blocks first: block 1's MFMAs run while block 0's weights and dS are
+// computed on the vector ALU.
+template <class E, int HS, bool DROP, bool KVL>
 __device__ __forceinline__ void dkdv_step_full(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
-                                      const float* Db, int qs0, int krow, int h, float c,
-                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R, uint32_t bh,
-                                      const Dropout& dr) {
+                                      const float* Db, const uint32_t* Bb, const uint16_t* KVb,
+                                      int kl, int qs0, int krow, int h, float c,
+                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R, int gl,
+                                      float zs) {
   using C = DkdvCfg<HS>;
-  if constexpr (DROP) {  // block by block: the generator's registers leave no room for both
-#pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) {
-      uint32_t w[2][2] = {};
-      dkdv_keep(qs0, qb, krow, h, bh, dr, w);
-      f32x16 s, dp;
-      dkdv_sdp<E, HS>(Qb, Gb, qb, L, R, s, dp);
-      dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R, w, dr.zs);
-    }
-  } else {
-    // S and dP of both blocks first: block 1's MFMAs run while block 0's
-    // weights and dS are computed on the vector ALU.
-    static_assert(C::QB == 2, "two query blocks per step");
-    const uint32_t w[2][2] = {};
-    f32x16 s0, dp0, s1, dp1;
-    dkdv_sdp<E, HS>(Qb, Gb, 0, L, R, s0, dp0);
-    dkdv_sdp<E, HS>(Qb, Gb, 1, L, R, s1, dp1);
-    dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, 0, qs0, krow, h, c, L, s0, dp0, R, w, dr.zs);
-    dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, 1, qs0, krow, h, c, L, s1, dp1, R, w, dr.zs);
-  }
+  static_assert(C::QB == 2, "two query blocks per step");
+  f32x16 s0, dp0, s1, dp1;
+  dkdv_sdp<E, HS, KVL>(Qb, Gb, KVb, kl, h, 0, L, R, s0, dp0);
+  dkdv_sdp<E, HS, KVL>(Qb, Gb, KVb, kl, h, 1, L, R, s1, dp1);
+  dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, Bb, 0, qs0, krow, h, c, L, s0, dp0, R, gl, zs);
+  dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, Bb, 1, qs0, krow, h, c, L, s1, dp1, R, gl, zs);
 }
 
 // A step that meets the diagonal: blocks wholly before this wavefront's keys
 // are skipped, the others masked.
-template <class E, int HS, bool DROP>
+template <class E, int HS, bool DROP, bool KVL>
 __device__ __forceinline__ void dkdv_step_diag(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
-                                      const float* Db, int qs0, int kw0, int krow, int h, float c,
-                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R, uint32_t bh,
-                                      const Dropout& dr) {
+                                      const float* Db, const uint32_t* Bb, const uint16_t* KVb,
+                                      int kl, int qs0, int kw0, int krow, int h, float c,
+                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R, int gl,
+                                      float zs) {
   using C = DkdvCfg<HS>;
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     if (kw0 > qs0 + qb * 32 + 31) continue;  // all of this wavefront's keys lie after the block
-    uint32_t w[2][2] = {};
-    if constexpr (DROP) dkdv_keep(qs0, qb, krow, h, bh, dr, w);
     f32x16 s, dp;
-    dkdv_sdp<E, HS>(Qb, Gb, qb, L, R, s, dp);
-    dkdv_grad<E, HS, true, DROP>(Qb, Gb, Lb, Db, qb, qs0, krow, h, c, L, s, dp, R, w, dr.zs);
+    dkdv_sdp<E, HS, KVL>(Qb, Gb, KVb, kl, h, qb, L, R, s, dp);
+    dkdv_grad<E, HS, true, DROP>(Qb, Gb, Lb, Db, Bb, qb, qs0, krow, h, c, L, s, dp, R, gl, zs);
   }
 }
 
@@ -290,14 +269,18 @@ template <class E, int HS, bool STRIDED, bool DROP>
 __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_OCC) void dkdv16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
-    const float* __restrict__ Dg, const float* __restrict__ L2g, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int BH, int H, int T, float scale, Layout li, Layout lo,
-    Layout lg, Dropout dr) {
+    const float* __restrict__ Dg, const float* __restrict__ L2g,
+    const uint64_t* __restrict__ keep, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    int BH, int H, int T, float scale, Layout li, Layout lo, Layout lg, Dropout dr) {
   using C = DkdvCfg<HS>;
+  constexpr int PER = C::PER + (DROP ? 1 : 0);
+  constexpr bool KVL = DROP || STRIDED;  // K, V fragments from LDS tiles
   __shared__ __attribute__((aligned(16))) uint16_t Qs[C::NS][C::BQ * HS];
   __shared__ __attribute__((aligned(16))) uint16_t Gs[C::NS][C::BQ * HS];
   __shared__ __attribute__((aligned(16))) float Ls[C::NS][C::BQ];
   __shared__ __attribute__((aligned(16))) float Ds[C::NS][C::BQ];
+  __shared__ __attribute__((aligned(16))) uint32_t Bs[DROP ? C::NS : 1][DROP ? C::KEEP_WORDS : 4];
+  __shared__ __attribute__((aligned(16))) uint16_t KVs[KVL ? 2 * C::BN * HS : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -318,13 +301,23 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
   const int kw0 = k0 + 32 * w;
   const int krow = kw0 + n;
   const float c = scale * kLog2e;
+  // Keep bits (DROP): this slice's ng x ng blocks of 8 bytes; gl = this
+  // lane's key group within the workgroup's 16.
+  const uint32_t ng = uint32_t(T + 7) >> 3;
+  const rsrc_t rb = make_rsrc(DROP ? keep + int64_t(bh) * ng * ng : keep, ng * ng * 8);
+  const int gl = (krow - k0) >> 3;
 
   DkdvRegs<HS> R;
+  if constexpr (KVL) {
+    dma_tile<HS, C::BN, C::NW>(rk, k0, rs, KVs, w, lane);
+    dma_tile<HS, C::BN, C::NW>(rv, k0, rs, KVs + C::BN * HS, w, lane);
+  } else {
 #pragma unroll
-  for (int ks = 0; ks < C::KSTEP; ++ks) {
-    const uint32_t off = uint32_t(krow * rs + 16 * ks + 8 * h) * 2;
-    R.kf[ks] = bload16(rk, off);
-    R.vf[ks] = bload16(rv, off);
+    for (int ks = 0; ks < C::KSTEP; ++ks) {
+      const uint32_t off = uint32_t(krow * rs + 16 * ks + 8 * h) * 2;
+      R.kf[ks] = bload16(rk, off);
+      R.vf[ks] = bload16(rv, off);
+    }
   }
 
 #pragma unroll
@@ -337,6 +330,16 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
     const uint32_t off = uint32_t(qt * C::BQ + w * QQ) * 4;
     dma_f32(rl, off, Ls[buf] + w * QQ, QQ, lane);
     dma_f32(rd, off, Ds[buf] + w * QQ, QQ, lane);
+    if constexpr (DROP) {
+      // Wavefront w: query octets 2w, 2w+1 of the step, 16 key groups each
+      // (lane: octet 2w + lane/8, groups 2 (lane%8) and +1; 16 bytes).
+      constexpr int KQ = C::KEEP_WORDS / C::NW;  // words per wavefront
+      const uint32_t qo = uint32_t(qt * (C::BQ / 8) + 2 * w + (lane >> 3));
+      if (lane < 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(Bs[buf] + w * KQ), 16,
+            (qo * ng + uint32_t(k0 >> 3) + 2u * uint32_t(lane & 7)) * 8, 0, 0, 0);
+    }
   };
 
   const int nqt = (T + C::BQ - 1) / C::BQ;
@@ -346,10 +349,14 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
 #pragma unroll
   for (int j = 0; j < C::NS - 1; ++j)
     if (j < nsteps) issue(qt0 + j, j);
-  wait_ring<C::NS, C::PER>(min(C::NS - 2, nsteps - 1));  // also the K, V fragments
+  wait_ring<C::NS, PER>(min(C::NS - 2, nsteps - 1));  // also the K, V fragments or tiles
   if constexpr (DsOf<E>::kConvert) {
+    if constexpr (KVL) {
+      dma_tile_to_f16<HS, C::BN, C::NW>(KVs, w, lane);
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEP; ++ks) R.kf[ks] = bf16x8_to_f16x8(R.kf[ks]);
+      for (int ks = 0; ks < C::KSTEP; ++ks) R.kf[ks] = bf16x8_to_f16x8(R.kf[ks]);
+    }
     dma_tile_to_f16<HS, C::BQ, C::NW>(Qs[0], w, lane);
   }
   __syncthreads();
@@ -360,13 +367,14 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
     constexpr int buf = decltype(bufc)::value;
     if (t + C::NS - 1 < nsteps) issue(qt0 + t + C::NS - 1, (buf + C::NS - 1) % C::NS);
     const int qs0 = (qt0 + t) * C::BQ;
+    const uint32_t* Bb = Bs[DROP ? buf : 0];
     if (qs0 < k0 + C::BN)
-      dkdv_step_diag<E, HS, DROP>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, kw0, krow, h, c, L, R,
-                                  uint32_t(bh), dr);
+      dkdv_step_diag<E, HS, DROP, KVL>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], Bb, KVs, krow - k0, qs0, kw0,
+                                  krow, h, c, L, R, gl, dr.zs);
     else
-      dkdv_step_full<E, HS, DROP>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], qs0, krow, h, c, L, R,
-                                  uint32_t(bh), dr);
-    wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nsteps - t - 2)));
+      dkdv_step_full<E, HS, DROP, KVL>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], Bb, KVs, krow - k0, qs0,
+                                  krow, h, c, L, R, gl, dr.zs);
+    wait_ring<C::NS, PER>(max(0, min(C::NS - 2, nsteps - t - 2)));
     if constexpr (DsOf<E>::kConvert)
       if (t + 1 < nsteps) dma_tile_to_f16<HS, C::BQ, C::NW>(Qs[(buf + 1) % C::NS], w, lane);
     __syncthreads();
@@ -408,8 +416,9 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
 // i.e. the kernel also accumulates M^T += K^T P^T (same K^T operands) and the
 // float32 row sums of dS~, and writes the exact D to the workspace for the
 // dK/dV kernel.  With dropout dS~ = P (Z dP - D~) and the same identities
-// hold (sum_j P Z dP = dO . O).  K and Q^T are fp16 (see DsOf): the K tile
-// is converted in place as it lands, Q^T once.
+// hold (sum_j P Z dP = dO . O); the kernel also stores each keep byte it
+// draws (query, 8-key group) for the dK/dV kernel (layout there).  K and Q^T
+// are fp16 (see DsOf): the K tile is converted in place as it lands, Q^T once.
 template <int HS>
 struct DqCfg {
   static constexpr int NW = 4;
@@ -442,7 +451,7 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
                                         f32x16 (&dqa)[HS / 32], f32x16 (&mka)[HS / 32],
                                         float& esum, const f32x16& negD, uint32_t qrow,
                                         uint32_t g0, uint32_t bh, const Dropout& dr,
-                                        F&& between) {
+                                        rsrc_t rb, uint32_t ng, F&& between) {
   using C = DqCfg<HS>;
   using Ed = typename DsOf<E>::T;
   constexpr int NKB = KIND == kDiagLo ? 1 : 2;  // 32-key blocks computed
@@ -455,7 +464,11 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) bits[kb][t] = keep_bits8(qrow, g0 + 4 * kb + 2 * t, bh, dr);
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t G = g0 + 4 * kb + 2 * t;
+        bits[kb][t] = keep_bits8(qrow, G, bh, dr);
+        if (G < ng) bstore1(rb, ((qrow >> 3) * ng + G) * 8 + (qrow & 7), bits[kb][t]);
+      }
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
@@ -504,9 +517,6 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
         dqa[db] = Ed::mfma(kt, dsp[kb][t], dqa[db]);
         mka[db] = Ed::mfma(kt, pp[kb][t], mka[db]);
       }
-  // Scheduling hint: spread the MFMAs over the step, each followed by vector
-  // ALU work and LDS reads of other blocks, instead of phase after phase.
-
 }
 
 template <class E, int HS, bool STRIDED, bool DROP>  // STRIDED, DROP as for the dK/dV kernel
@@ -514,8 +524,8 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dO, const float* __restrict__ lse, float* __restrict__ Dg,
-    float* __restrict__ L2g, uint16_t* __restrict__ dq, int BH, int H, int T, float scale,
-    Layout li, Layout lo, Layout lg, Dropout dr) {
+    float* __restrict__ L2g, uint64_t* __restrict__ keep, uint16_t* __restrict__ dq, int BH,
+    int H, int T, float scale, Layout li, Layout lo, Layout lg, Dropout dr) {
   using C = DqCfg<HS>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[C::NS][C::BN * HS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[C::NS][C::BN * HS];
@@ -539,6 +549,9 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
   const int qrow = q0 + n;
   const int dn = n - 8 * h;
   const float c = scale * kLog2e;
+  // Keep bytes (DROP): this slice's ng x ng blocks of 8 bytes.
+  const uint32_t ng = uint32_t(T + 7) >> 3;
+  const rsrc_t rb = make_rsrc(DROP ? keep + int64_t(bh) * ng * ng : keep, ng * ng * 8);
 
   auto issue = [&](int kt, int buf) {
     dma_tile<HS, C::BN, C::NW>(rk, kt * C::BN, rs, Ks[buf], w, lane);
@@ -608,13 +621,13 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
     if (q0 < T && key0 <= q0) {
       if (key0 == q0)
         dq_step<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
-                                      negD, uq, g0, ub, dr, between);
+                                      negD, uq, g0, ub, dr, rb, ng, between);
       else if (key0 + 32 == q0)
         dq_step<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
-                                      negD, uq, g0, ub, dr, between);
+                                      negD, uq, g0, ub, dr, rb, ng, between);
       else
         dq_step<E, HS, kFull, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
-                                    negD, uq, g0, ub, dr, between);
+                                    negD, uq, g0, ub, dr, rb, ng, between);
     } else {
       between();
     }
@@ -658,9 +671,10 @@ hipError_t pre16_launch(const uint16_t* o, const uint16_t* dO, const float* lse,
 
 template <class E>
 hipError_t dkdv16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
-                         uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
-                         Layout lo, Layout lg, const Dropout& dr, hipStream_t s) {
+                         const uint16_t* dO, const float* D, const float* L2,
+                         const uint64_t* keep, uint16_t* dk, uint16_t* dv, int BH, int H, int T,
+                         int hs, float scale, Layout li, Layout lo, Layout lg, const Dropout& dr,
+                         hipStream_t s) {
   const int bn = DkdvCfg<64>::BN;
   const dim3 grid(unsigned(((T + bn - 1) / bn) * BH));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
@@ -670,15 +684,16 @@ hipError_t dkdv16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v
                     : (strided ? dkdv16_kernel<E, 32, true, D> : dkdv16_kernel<E, 32, false, D>);
   };
   auto kern = dr.thr != 0 ? pick(std::true_type{}) : pick(std::false_type{});
-  return launch(kern, grid, dim3(kThreads), s, q, k, v, dO, D, L2, dk, dv, BH, H, T, scale, li, lo,
-                lg, dr);
+  return launch(kern, grid, dim3(kThreads), s, q, k, v, dO, D, L2, keep, dk, dv, BH, H, T, scale,
+                li, lo, lg, dr);
 }
 
 template <class E>
 hipError_t dq16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                       float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
-                       Layout li, Layout lo, Layout lg, const Dropout& dr, hipStream_t s) {
+                       float* L2, uint64_t* keep, uint16_t* dq, int BH, int H, int T, int hs,
+                       float scale, Layout li, Layout lo, Layout lg, const Dropout& dr,
+                       hipStream_t s) {
   const int bm = DqCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
@@ -688,8 +703,8 @@ hipError_t dq16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     : (strided ? dq16_kernel<E, 32, true, D> : dq16_kernel<E, 32, false, D>);
   };
   auto kern = dr.thr != 0 ? pick(std::true_type{}) : pick(std::false_type{});
-  return launch(kern, grid, dim3(kThreads), s, q, k, v, o, dO, lse, D, L2, dq, BH, H, T, scale, li,
-                lo, lg, dr);
+  return launch(kern, grid, dim3(kThreads), s, q, k, v, o, dO, lse, D, L2, keep, dq, BH, H, T,
+                scale, li, lo, lg, dr);
 }
 }  // namespace
 
@@ -701,22 +716,27 @@ hipError_t h16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, 
 }
 
 hipError_t h16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        const uint16_t* dO, const float* D, const float* L2, uint16_t* dk,
-                        uint16_t* dv, int BH, int H, int T, int hs, float scale, Layout li,
-                        Layout lo, Layout lg, const Dropout& dr, bool f16, hipStream_t s) {
+                        const uint16_t* dO, const float* D, const float* L2,
+                        const uint64_t* keep, uint16_t* dk, uint16_t* dv, int BH, int H, int T,
+                        int hs, float scale, Layout li, Layout lo, Layout lg, const Dropout& dr,
+                        bool f16, hipStream_t s) {
   if (f16)
-    return dkdv16_launch<F16>(q, k, v, dO, D, L2, dk, dv, BH, H, T, hs, scale, li, lo, lg, dr, s);
-  return dkdv16_launch<Bf16>(q, k, v, dO, D, L2, dk, dv, BH, H, T, hs, scale, li, lo, lg, dr, s);
+    return dkdv16_launch<F16>(q, k, v, dO, D, L2, keep, dk, dv, BH, H, T, hs, scale, li, lo, lg,
+                              dr, s);
+  return dkdv16_launch<Bf16>(q, k, v, dO, D, L2, keep, dk, dv, BH, H, T, hs, scale, li, lo, lg,
+                             dr, s);
 }
 
 hipError_t h16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                      float* L2, uint16_t* dq, int BH, int H, int T, int hs, float scale,
-                      Layout li, Layout lo, Layout lg, const Dropout& dr, bool f16,
+                      float* L2, uint64_t* keep, uint16_t* dq, int BH, int H, int T, int hs,
+                      float scale, Layout li, Layout lo, Layout lg, const Dropout& dr, bool f16,
                       hipStream_t s) {
   if (f16)
-    return dq16_launch<F16>(q, k, v, o, dO, lse, D, L2, dq, BH, H, T, hs, scale, li, lo, lg, dr, s);
-  return dq16_launch<Bf16>(q, k, v, o, dO, lse, D, L2, dq, BH, H, T, hs, scale, li, lo, lg, dr, s);
+    return dq16_launch<F16>(q, k, v, o, dO, lse, D, L2, keep, dq, BH, H, T, hs, scale, li, lo, lg,
+                            dr, s);
+  return dq16_launch<Bf16>(q, k, v, o, dO, lse, D, L2, keep, dq, BH, H, T, hs, scale, li, lo, lg,
+                           dr, s);
 }
 
 }  // namespace gattn

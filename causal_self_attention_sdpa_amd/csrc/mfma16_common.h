@@ -126,6 +126,9 @@ __device__ inline void bstore8(rsrc_t r, uint32_t off, u32x2 v) {
 __device__ inline void bstoref(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
 }
+__device__ inline void bstore1(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8(static_cast<unsigned char>(v), r, off, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // Swizzled LDS tiles.  A tile holds rows of HS bf16 back to back (HS*2 bytes,

@@ -262,7 +262,9 @@ int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, 
  * (low half first) of word (j & 7) >> 1, and keep(i, j) = u(i, j) >= t.  The
  * same (seed, offset) draws the same mask in the forward, the backward and
  * gattn_dropout_mask; give each layer and step its own (seed, offset).
- * The mask is recomputed where needed, never stored.
+ * The forward draws the mask as it goes and stores none of it; the 16-bit
+ * backward draws it once (in its dQ pass) and keeps it as bits in the
+ * workspace for its dK/dV pass.
  *
  * gattn_fwd_dropout: as gattn_fwd_strided (strides NULL = contiguous) with
  * dropout of probability p.  p = 0 (t = 0) runs exactly gattn_fwd_strided.
@@ -274,9 +276,23 @@ int gattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, floa
                       const int64_t* o_strides, hipStream_t stream);
 
 /*
+ * gattn_bwd_dropout_workspace_bytes: workspace bytes gattn_bwd_dropout needs
+ * for this shape and p: gattn_bwd_workspace_bytes() plus, for bf16 and fp16
+ * with p rounding to a nonzero threshold, B*H*ceil(T/8)^2*8 bytes (one bit
+ * per query-key pair of each (b, h) slice, 256-byte rounded).  0 for
+ * arguments gattn_bwd_dropout rejects as INVALID_ARG or UNSUPPORTED (bad
+ * shape or p; 16-bit with dropout and T > 131064).
+ */
+size_t gattn_bwd_dropout_workspace_bytes(int B, int H, int T, int hs, int dtype, float p);
+
+/*
  * gattn_bwd_dropout: the backward of gattn_fwd_dropout with the same p, seed
- * and offset (o and lse as that forward wrote them); arguments, workspace and
- * strides as gattn_bwd_strided.  p = 0 runs exactly gattn_bwd_strided.
+ * and offset (o and lse as that forward wrote them); arguments and strides
+ * as gattn_bwd_strided; workspace: at least
+ * gattn_bwd_dropout_workspace_bytes() bytes, 256-byte aligned (contents need
+ * no initialisation; GATTN_ERR_WORKSPACE if smaller).  p = 0 runs exactly
+ * gattn_bwd_strided.  INVALID_ARG also for p as in gattn_fwd_dropout and,
+ * for bf16 and fp16 with dropout, T > 131064.
  */
 int gattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int T, int hs,

@@ -239,10 +239,40 @@ def test_dropout_validation(lib):
     assert bwd(lse=None) == INVALID                              # the backward needs lse
     assert bwd(ws=None) == WORKSPACE
     assert bwd(wsb=16) == WORKSPACE
+    # The 16-bit backward with dropout also needs room for the keep bits.
+    base = ga.gattn_bwd_workspace_bytes(2, 3, 100, 64, ga.BF16)
+    assert bwd(wsb=base) == WORKSPACE
+    assert bwd(wsb=ga.gattn_bwd_dropout_workspace_bytes(2, 3, 100, 64, ga.BF16, 0.1) - 1) == WORKSPACE
+    big_t = 8 * 16383 + 1   # ceil(T / 8) past the keep-bit addressing limit
+    assert lib.gattn_bwd_dropout(P, P, P, P, P, P, P, P, P, 1, 1, big_t, 64, 0.125, 1, 0.1, 7, 1,
+                                 P, 1 << 40, None, None, None, None) == INVALID
     assert bwd(sg=_st(-1, 64, 64)) == INVALID
     assert mask(keep=None) == INVALID
     assert mask(T=0) == INVALID
     assert mask(B=1 << 10, H=1 << 10, T=1 << 10) == INVALID     # 2^40 bytes
+
+
+def test_dropout_workspace_bytes(lib):
+    """The dropout backward's workspace: the plain backward's, plus for bf16
+    and fp16 one bit per query-key pair of every slice (ceil(T/8)^2 blocks of
+    8 bytes per (b, h), 256-byte rounded)."""
+    def need(B=2, H=3, T=100, hs=64, dt=ga.BF16, p=0.1):
+        return ga.gattn_bwd_dropout_workspace_bytes(B, H, T, hs, dt, p)
+
+    base = ga.gattn_bwd_workspace_bytes(2, 3, 100, 64, ga.BF16)
+    keep = -(-(2 * 3 * 13 * 13 * 8) // 256) * 256  # ceil(100 / 8) = 13 groups
+    assert need() == base + keep
+    assert need(dt=ga.F16) == base + keep
+    assert need(dt=ga.F32) == ga.gattn_bwd_workspace_bytes(2, 3, 100, 64, ga.F32)
+    assert need(p=0.0) == base
+    assert need(p=2.0 ** -18) == base             # rounds to threshold 0: no dropout
+    assert need(T=8, B=1, H=1) == ga.gattn_bwd_workspace_bytes(1, 1, 8, 64, ga.BF16) + 256
+    for bad in (-0.1, 1.0, float("nan")):
+        assert need(p=bad) == 0
+    assert need(hs=48) == 0 and need(B=0) == 0
+    assert need(B=1, H=1, T=8 * 16383) > 0
+    assert need(B=1, H=1, T=8 * 16383 + 1) == 0
+    assert need(B=1, H=1, T=8 * 16383 + 1, dt=ga.F32) > 0
 
 
 def test_probe_validation(lib):

@@ -247,6 +247,35 @@ def test_same_seed_reproduces_other_offsets_differ():
     assert np.array_equal(a[4], c[4])  # lse is that of the softmax before dropout
 
 
+@pytest.mark.parametrize("dtype,T,hs", [("bf16", 200, 64), ("f16", 333, 32)])
+def test_workspace_contents_do_not_matter(dtype, T, hs):
+    """The 16-bit backward keeps the dQ pass's keep decisions in the workspace
+    for the dK/dV pass, which also reads blocks at masked (above-diagonal)
+    positions that nothing wrote: a workspace of zeros, of 0xFF bytes, or
+    left from another seed gives the same gradients bit for bit."""
+    import torch
+    import causal_self_attention_sdpa_amd as ga
+    B, H = 2, 3
+    x = inputs(B, H, T, hs, dtype, seed=107, workload="dropout-ws")
+    s = default_scale(hs)
+    t = {n: to_dev(a, dtype) for n, a in x.items()}
+    o, lse = ga.attention_forward_dropout(t["q"], t["k"], t["v"], 0.25, 31, 2, scale=s)
+    n = ga.gattn_bwd_dropout_workspace_bytes(B, H, T, hs, ga.BF16 if dtype == "bf16" else ga.F16,
+                                             0.25)
+    outs = []
+    for fill in (0x00, 0xFF, None):
+        ws = torch.full((n,), fill if fill is not None else 0, dtype=torch.uint8, device="cuda")
+        if fill is None:  # left over from a call with another seed and offset
+            ga.attention_backward_dropout(t["q"], t["k"], t["v"], o, t["do"], lse, 0.25, 77, 5,
+                                          scale=s, workspace=ws)
+        outs.append(ga.attention_backward_dropout(t["q"], t["k"], t["v"], o, t["do"], lse, 0.25,
+                                                  31, 2, scale=s, workspace=ws))
+    torch.cuda.synchronize()
+    for other in outs[1:]:
+        for name, a, b in zip(("dq", "dk", "dv"), outs[0], other):
+            assert torch.equal(a, b), name
+
+
 def test_fused_qkv_layout_equals_contiguous_bitwise():
     """Dropout through strided (B, T, 3C) / (B, T, C) views gives the same bits
     as the contiguous call."""
@@ -268,8 +297,8 @@ def test_fused_qkv_layout_equals_contiguous_bitwise():
     ga.gattn_fwd_dropout(q, k, v, y4, lse, s, p, 21, 4)
     dqkv = torch.empty_like(qkv)
     g4 = dqkv.view(B, T, 3, H, hs)
-    ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(ga.gattn_bwd_dropout_workspace_bytes(B, H, T, hs, ga.BF16, p),
+                     dtype=torch.uint8, device="cuda")
     ga.gattn_bwd_dropout(q, k, v, y4, dy.view(B, T, H, hs).transpose(1, 2), lse,
                          *(g4[:, :, j].transpose(1, 2) for j in range(3)), s, p, 21, 4, ws)
     torch.cuda.synchronize()
