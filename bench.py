@@ -483,9 +483,14 @@ def main() -> int:
             t[g] = torch.empty_like(t["q"])
         layers.append(t)
     drop = args.dropout > 0.0
-    wsn = (ga.gattn_bwd_dropout_workspace_bytes(B, H, T, hs, dcode, args.dropout) if drop
-           else ga.gattn_bwd_workspace_bytes(B, H, T, hs, dcode))
-    ws = torch.empty(wsn, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, dcode), dtype=torch.uint8,
+                     device=dev)
+    if drop:
+        # Each layer's forward stores its keep decisions (one bit per causal
+        # pair, saved for the backward like lse); its backward reads them.
+        for t in layers:
+            t["keep"] = torch.empty(ga.gattn_dropout_keep_bytes(B, H, T), dtype=torch.uint8,
+                                    device=dev)
     stream = torch.cuda.current_stream()
     timer = HipTimer()
     if drop and args.layout != "contiguous":
@@ -509,11 +514,12 @@ def main() -> int:
             call.append({
                 "fwd_dropout": (lib.gattn_fwd_dropout,
                                 (p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["lse"]), B, H, T,
-                                 hs, scale, dcode, pd, seed, off, None, None, sp)),
+                                 hs, scale, dcode, pd, seed, off, p(t["keep"]), None, None, sp)),
                 "bwd_dropout": (lib.gattn_bwd_dropout,
                                 (p(t["q"]), p(t["k"]), p(t["v"]), p(t["o"]), p(t["do"]),
                                  p(t["lse"]), p(t["dq"]), p(t["dk"]), p(t["dv"]), B, H, T, hs,
-                                 scale, dcode, pd, seed, off, p(ws), wsb, None, None, None, sp)),
+                                 scale, dcode, pd, seed, off, p(t["keep"]), p(ws), wsb, None, None,
+                                 None, sp)),
             })
             continue
         call.append({
@@ -688,6 +694,8 @@ def main() -> int:
         "config": {"workload": W["label"] + (f", attention dropout p={args.dropout}" if drop else ""),
                    "B": B, "H": H, "T": T, "hs": hs, "layers": L, "qkv_scale": W["qkv_scale"],
                    "dropout": args.dropout,
+                   **({"dropout_mask": "drawn by the forward, stored as 1 bit per query-key "
+                                       "pair, read by the backward"} if drop else {}),
                    "flop_count": "causal pairs, fwd 4*hs, bwd 8*hs per pair",
                    "parallelism": "single GPU"},
         "value_flashattention_count": round(value_fa, 3),

@@ -40,6 +40,7 @@ from ._binding import (  # noqa: F401
     gattn_bwd_workspace_bytes,
     gattn_fwd,
     gattn_fwd_decode,
+    gattn_dropout_keep_bytes,
     gattn_dropout_mask,
     gattn_fwd_decode_workspace_bytes,
     gattn_fwd_dropout,

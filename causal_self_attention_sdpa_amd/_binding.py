@@ -62,10 +62,12 @@ def load_library():
     lib.gattn_fwd_decode.argtypes = [vp] * 5 + [i, i, i, i, i, f, i, vp, vp, vp, vp, sz, vp]
     lib.gattn_fwd_decode.restype = i
     u64, u32 = ctypes.c_uint64, ctypes.c_uint32
-    lib.gattn_fwd_dropout.argtypes = [vp] * 5 + [i, i, i, i, f, i, f, u64, u32, vp, vp, vp]
+    lib.gattn_fwd_dropout.argtypes = [vp] * 5 + [i, i, i, i, f, i, f, u64, u32, vp, vp, vp, vp]
     lib.gattn_fwd_dropout.restype = i
-    lib.gattn_bwd_dropout.argtypes = ([vp] * 9 + [i, i, i, i, f, i, f, u64, u32, vp, sz]
+    lib.gattn_bwd_dropout.argtypes = ([vp] * 9 + [i, i, i, i, f, i, f, u64, u32, vp, vp, sz]
                                       + [vp, vp, vp, vp])
+    lib.gattn_dropout_keep_bytes.argtypes = [i, i, i]
+    lib.gattn_dropout_keep_bytes.restype = sz
     lib.gattn_bwd_dropout.restype = i
     lib.gattn_bwd_dropout_workspace_bytes.argtypes = [i, i, i, i, i, f]
     lib.gattn_bwd_dropout_workspace_bytes.restype = sz
@@ -303,10 +305,25 @@ def attention_decode(q, k, v, scale=None, need_lse: bool = False, workspace=None
     return o, lse
 
 
+def gattn_dropout_keep_bytes(B: int, H: int, T: int) -> int:
+    return int(load_library().gattn_dropout_keep_bytes(B, H, T))
+
+
+def _keep_arg(keep, B, H, T):
+    if keep is None:
+        return None
+    need = gattn_dropout_keep_bytes(B, H, T)
+    if keep.dtype != _torch().uint8 or not keep.is_contiguous() or keep.numel() < need:
+        raise ValueError(f"keep: a contiguous uint8 device tensor of at least {need} bytes")
+    return _dev(keep, "keep")
+
+
 def gattn_fwd_dropout(q, k, v, o, lse, scale: float, p: float, seed: int, offset: int,
-                      stream=None) -> None:
+                      stream=None, keep=None) -> None:
     """As gattn_fwd_strided with attention dropout of probability p; the
-    mask is drawn from (seed, offset) as the C header defines."""
+    mask is drawn from (seed, offset) as the C header defines.  keep: None or
+    a uint8 tensor of gattn_dropout_keep_bytes() bytes the 16-bit kernels
+    store the keep decisions in, for gattn_bwd_dropout."""
     lib = load_library()
     B, H, T, hs = _shape4(q)
     dt = _dtype_code(q)
@@ -314,7 +331,7 @@ def gattn_fwd_dropout(q, k, v, o, lse, scale: float, p: float, seed: int, offset
     ov = _view(o, "o", q.shape, q.dtype)
     lp = None if lse is None else _dev(lse, "lse", (B, H, T), _torch().float32)
     _check(lib.gattn_fwd_dropout(*(x for x, _ in qkv), ov[0], lp, B, H, T, hs, float(scale), dt,
-                                 float(p), int(seed), int(offset),
+                                 float(p), int(seed), int(offset), _keep_arg(keep, B, H, T),
                                  _strides_arg(qkv, "q, k, v"), _strides_arg([ov], "o"),
                                  _stream(stream)), "gattn_fwd_dropout")
 
@@ -325,9 +342,9 @@ def gattn_bwd_dropout_workspace_bytes(B: int, H: int, T: int, hs: int, dtype: in
 
 
 def gattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, scale: float, p: float, seed: int,
-                      offset: int, workspace, stream=None) -> None:
+                      offset: int, workspace, stream=None, keep=None) -> None:
     """Backward of gattn_fwd_dropout (same p, seed, offset); strided views as
-    gattn_bwd_strided."""
+    gattn_bwd_strided; keep: None or the keep tensor that forward filled."""
     lib = load_library()
     B, H, T, hs = _shape4(q)
     dt = _dtype_code(q)
@@ -339,7 +356,7 @@ def gattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, scale: float, p: float, s
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.gattn_bwd_dropout(*(x for x, _ in qkv), *(x for x, _ in od), lp,
                                  *(x for x, _ in gr), B, H, T, hs, float(scale), dt, float(p),
-                                 int(seed), int(offset), ws, nbytes,
+                                 int(seed), int(offset), _keep_arg(keep, B, H, T), ws, nbytes,
                                  _strides_arg(qkv, "q, k, v"), _strides_arg(od, "o, dO"),
                                  _strides_arg(gr, "dq, dk, dv"), _stream(stream)),
            "gattn_bwd_dropout")
@@ -355,28 +372,35 @@ def gattn_dropout_mask(keep, B: int, H: int, T: int, p: float, seed: int, offset
 
 
 def attention_forward_dropout(q, k, v, p: float, seed: int, offset: int = 0, scale=None,
-                              need_lse: bool = True, stream=None):
-    """Returns (o, lse) with attention dropout; lse is None if not needed."""
+                              need_lse: bool = True, stream=None, return_keep: bool = False):
+    """Returns (o, lse) with attention dropout; lse is None if not needed.
+    return_keep: also return the keep-decision bits the forward stored
+    (uint8 tensor, for attention_backward_dropout), as (o, lse, keep)."""
     torch = _torch()
     B, H, T, hs = _shape4(q)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if need_lse else None
-    gattn_fwd_dropout(q, k, v, o, lse, _default_scale(hs, scale), p, seed, offset, stream)
-    return o, lse
+    keep = None
+    if return_keep:
+        keep = torch.empty(gattn_dropout_keep_bytes(B, H, T), dtype=torch.uint8, device=q.device)
+    gattn_fwd_dropout(q, k, v, o, lse, _default_scale(hs, scale), p, seed, offset, stream, keep)
+    return (o, lse, keep) if return_keep else (o, lse)
 
 
 def attention_backward_dropout(q, k, v, o, dO, lse, p: float, seed: int, offset: int = 0,
-                               scale=None, workspace=None, stream=None):
+                               scale=None, workspace=None, stream=None, keep=None):
     """Returns (dq, dk, dv) of attention_forward_dropout with the same p, seed,
-    offset; allocates the workspace unless one is given."""
+    offset (and its keep bits if it returned them); allocates the workspace
+    unless one is given."""
     torch = _torch()
     B, H, T, hs = _shape4(q)
     if workspace is None:
-        n = gattn_bwd_dropout_workspace_bytes(B, H, T, hs, _dtype_code(q), p)
+        n = (gattn_bwd_workspace_bytes(B, H, T, hs, _dtype_code(q)) if keep is not None
+             else gattn_bwd_dropout_workspace_bytes(B, H, T, hs, _dtype_code(q), p))
         workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     gattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, _default_scale(hs, scale), p, seed,
-                      offset, workspace, stream)
+                      offset, workspace, stream, keep)
     return dq, dk, dv
 
 

@@ -102,7 +102,7 @@ float* ws_L2(void* ws, int B, int H, int T) {
 // Implementations on layouts (arguments already validated).
 int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int T, int hs, float scale, int dtype, gattn::Layout li, gattn::Layout lo,
-             const gattn::Dropout& dr, hipStream_t stream) {
+             const gattn::Dropout& dr, hipStream_t stream, void* keep = nullptr) {
   const int BH = B * H;
   if (dtype == GATTN_F32)
     return status_of(gattn::f32_fwd(static_cast<const float*>(q), static_cast<const float*>(k),
@@ -110,7 +110,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, i
                                     H, T, T, hs, scale, li, li, lo, dr, stream));
   return status_of(gattn::h16_fwd(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                   static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse,
-                                  BH, H, T, hs, scale, li, lo, dr, dtype == GATTN_F16, stream));
+                                  static_cast<uint64_t*>(keep), BH, H, T, hs, scale, li, lo, dr,
+                                  dtype == GATTN_F16, stream));
 }
 
 int pre_impl(const void* o, const void* dO, const float* lse, int B, int H, int T, int hs,
@@ -130,10 +131,12 @@ uint64_t* ws_keep(void* ws, int B, int H, int T) {
   return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + 2 * ws_part_bytes(B, H, T));
 }
 
+// keep (dropout, 16-bit): NULL = the dQ pass draws the decisions and keeps
+// them in the workspace; else the bits gattn_fwd_dropout stored.
 int dq_impl(const void* q, const void* k, const void* v, const void* o, const void* dO,
             const float* lse, void* dq, int B, int H, int T, int hs, float scale, int dtype,
             void* workspace, gattn::Layout li, gattn::Layout lo, gattn::Layout lg,
-            const gattn::Dropout& dr, hipStream_t stream) {
+            const gattn::Dropout& dr, hipStream_t stream, const void* keep = nullptr) {
   float* D = ws_D(workspace);
   float* L2 = ws_L2(workspace, B, H, T);
   if (dtype == GATTN_F32) {
@@ -147,14 +150,17 @@ int dq_impl(const void* q, const void* k, const void* v, const void* o, const vo
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o),
       static_cast<const uint16_t*>(dO), lse, D, L2,
-      dr.thr != 0 ? ws_keep(workspace, B, H, T) : nullptr, static_cast<uint16_t*>(dq), B * H, H,
-      T, hs, scale, li, lo, lg, dr, dtype == GATTN_F16, stream));
+      dr.thr == 0 ? nullptr
+                  : keep ? static_cast<uint64_t*>(const_cast<void*>(keep))
+                         : ws_keep(workspace, B, H, T),
+      keep != nullptr, static_cast<uint16_t*>(dq), B * H, H, T, hs, scale, li, lo, lg, dr,
+      dtype == GATTN_F16, stream));
 }
 
 int dkdv_impl(const void* q, const void* k, const void* v, const void* dO, void* dk, void* dv,
               int B, int H, int T, int hs, float scale, int dtype, void* workspace,
               gattn::Layout li, gattn::Layout lo, gattn::Layout lg, const gattn::Dropout& dr,
-              hipStream_t stream) {
+              hipStream_t stream, const void* keep = nullptr) {
   const float* D = ws_D(workspace);
   const float* L2 = ws_L2(workspace, B, H, T);
   if (dtype == GATTN_F32)
@@ -165,7 +171,9 @@ int dkdv_impl(const void* q, const void* k, const void* v, const void* dO, void*
   return status_of(gattn::h16_bwd_dkdv(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(dO), D, L2,
-      dr.thr != 0 ? ws_keep(workspace, B, H, T) : nullptr, static_cast<uint16_t*>(dk),
+      dr.thr == 0 ? nullptr
+                  : keep ? static_cast<const uint64_t*>(keep) : ws_keep(workspace, B, H, T),
+      static_cast<uint16_t*>(dk),
       static_cast<uint16_t*>(dv), B * H, H, T, hs, scale, li, lo, lg, dr, dtype == GATTN_F16,
       stream));
 }
@@ -237,6 +245,13 @@ size_t gattn_bwd_workspace_bytes(int B, int H, int T, int hs, int dtype) {
   return 2 * ws_part_bytes(B, H, T);
 }
 
+size_t gattn_dropout_keep_bytes(int B, int H, int T) {
+  if (B < 1 || H < 1 || T < 1 || (int64_t(T) + 7) / 8 > gattn::kKeepMaxGroups) return 0;
+  const int64_t ng = (int64_t(T) + 7) / 8;
+  if (int64_t(B) * H > (int64_t(1) << 40) / (ng * ng * 8)) return 0;
+  return gattn::ws_keep_bytes(B, H, T);
+}
+
 size_t gattn_bwd_dropout_workspace_bytes(int B, int H, int T, int hs, int dtype, float p) {
   gattn::Dropout dr;
   if (check_shape(B, H, T, hs, dtype) != GATTN_OK || dropout_of(p, 0, 0, dr) != GATTN_OK) return 0;
@@ -265,15 +280,17 @@ int gattn_fwd_strided(const void* q, const void* k, const void* v, void* o, floa
 
 int gattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int T, int hs, float scale, int dtype, float p, uint64_t seed,
-                      uint32_t offset, const int64_t* qkv_strides, const int64_t* o_strides,
-                      hipStream_t stream) {
+                      uint32_t offset, void* keep, const int64_t* qkv_strides,
+                      const int64_t* o_strides, hipStream_t stream) {
   if (int st = check_fwd(q, k, v, o, lse, B, H, T, hs, scale, dtype)) return st;
   gattn::Dropout dr;
   if (int st = dropout_of(p, seed, offset, dr)) return st;
+  if (keep != nullptr && (!aligned(keep, 16) || gattn_dropout_keep_bytes(B, H, T) == 0))
+    return GATTN_ERR_INVALID_ARG;
   gattn::Layout li, lo;
   if (int st = layout_of(qkv_strides, H, T, hs, dtype, li)) return st;
   if (int st = layout_of(o_strides, H, T, hs, dtype, lo)) return st;
-  return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, li, lo, dr, stream);
+  return fwd_impl(q, k, v, o, lse, B, H, T, hs, scale, dtype, li, lo, dr, stream, keep);
 }
 
 int gattn_probe_mfma_bf16(float* sink, int blocks, int iters, hipStream_t stream) {
@@ -421,9 +438,9 @@ int gattn_bwd_strided(const void* q, const void* k, const void* v, const void* o
 int gattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int T, int hs,
                       float scale, int dtype, float p, uint64_t seed, uint32_t offset,
-                      void* workspace, size_t workspace_bytes, const int64_t* qkv_strides,
-                      const int64_t* o_strides, const int64_t* grad_strides,
-                      hipStream_t stream) {
+                      const void* keep, void* workspace, size_t workspace_bytes,
+                      const int64_t* qkv_strides, const int64_t* o_strides,
+                      const int64_t* grad_strides, hipStream_t stream) {
   if (int st = check_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, T, hs, scale, dtype, workspace,
                          workspace_bytes))
     return st;
@@ -431,17 +448,21 @@ int gattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o
   if (int st = dropout_of(p, seed, offset, dr)) return st;
   if (dtype != GATTN_F32 && dr.thr != 0 && (int64_t(T) + 7) / 8 > gattn::kKeepMaxGroups)
     return GATTN_ERR_INVALID_ARG;
-  if (workspace_bytes < gattn_bwd_dropout_workspace_bytes(B, H, T, hs, dtype, p))
+  if (keep != nullptr && (!aligned(keep, 16) || gattn_dropout_keep_bytes(B, H, T) == 0))
+    return GATTN_ERR_INVALID_ARG;
+  if (dtype == GATTN_F32 || dr.thr == 0) keep = nullptr;  // the float32 path draws its own
+  if (keep == nullptr &&
+      workspace_bytes < gattn_bwd_dropout_workspace_bytes(B, H, T, hs, dtype, p))
     return GATTN_ERR_WORKSPACE;
   gattn::Layout li, lo, lg;
   if (int st = layout_of(qkv_strides, H, T, hs, dtype, li)) return st;
   if (int st = layout_of(o_strides, H, T, hs, dtype, lo)) return st;
   if (int st = layout_of(grad_strides, H, T, hs, dtype, lg)) return st;
   if (int st = dq_impl(q, k, v, o, dO, lse, dq, B, H, T, hs, scale, dtype, workspace, li, lo, lg,
-                       dr, stream))
+                       dr, stream, keep))
     return st;
   return dkdv_impl(q, k, v, dO, dk, dv, B, H, T, hs, scale, dtype, workspace, li, lo, lg, dr,
-                   stream);
+                   stream, keep);
 }
 
 }  // extern "C"

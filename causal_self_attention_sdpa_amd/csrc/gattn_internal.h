@@ -166,9 +166,11 @@ hipError_t f32_bwd_dq(const float* q, const float* k, const float* v, const floa
                       hipStream_t s);
 
 // ---- 16-bit path: bf16 (f16 = false) or fp16 (f16 = true), hs in {32, 64}; MFMA ----
+// keep: with dropout, NULL or the keep-bit blocks (ws_keep_bytes) to store
+// the decisions in for the backward.
 hipError_t h16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                   float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
-                   const Dropout& dr, bool f16, hipStream_t s);
+                   float* lse, uint64_t* keep, int BH, int H, int T, int hs, float scale,
+                   Layout li, Layout lo, const Dropout& dr, bool f16, hipStream_t s);
 // Forward of the newest Tq tokens against Tk >= Tq keys, split over the key
 // range (partials in opart / lpart, then merged into o and lse).
 hipError_t h16_fwd_decode(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
@@ -184,7 +186,8 @@ hipError_t h16_bwd_pre(const uint16_t* o, const uint16_t* dO, const float* lse, 
                        float* L2, int BH, int H, int T, int hs, Layout lo, bool f16,
                        hipStream_t s);
 // keep: with dropout (dr.thr != 0) the keep-bit blocks, ws_keep_bytes(BH, T)
-// bytes: written by h16_bwd_dq, read by h16_bwd_dkdv; unused otherwise.
+// bytes: written by h16_bwd_dq (or, keep_stored, already written by the
+// forward and read by h16_bwd_dq too), read by h16_bwd_dkdv; unused otherwise.
 hipError_t h16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* dO, const float* D, const float* L2,
                         const uint64_t* keep, uint16_t* dk, uint16_t* dv, int BH, int H, int T,
@@ -192,8 +195,8 @@ hipError_t h16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         bool f16, hipStream_t s);
 hipError_t h16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                      float* L2, uint64_t* keep, uint16_t* dq, int BH, int H, int T, int hs,
-                      float scale, Layout li, Layout lo, Layout lg, const Dropout& dr, bool f16,
-                      hipStream_t s);
+                      float* L2, uint64_t* keep, bool keep_stored, uint16_t* dq, int BH, int H,
+                      int T, int hs, float scale, Layout li, Layout lo, Layout lg,
+                      const Dropout& dr, bool f16, hipStream_t s);
 
 }  // namespace gattn

@@ -416,9 +416,15 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
 // i.e. the kernel also accumulates M^T += K^T P^T (same K^T operands) and the
 // float32 row sums of dS~, and writes the exact D to the workspace for the
 // dK/dV kernel.  With dropout dS~ = P (Z dP - D~) and the same identities
-// hold (sum_j P Z dP = dO . O); the kernel also stores each keep byte it
-// draws (query, 8-key group) for the dK/dV kernel (layout there).  K and Q^T
-// are fp16 (see DsOf): the K tile is converted in place as it lands, Q^T once.
+// hold (sum_j P Z dP = dO . O).  The keep decisions either are drawn here
+// and each byte (query, 8-key group) is stored for the dK/dV kernel
+// (DROP == kDropDraw; layout there), or come from the bytes the forward
+// stored (kDropRead), DMA'd into LDS step by step like the K and V tiles.
+// K and Q^T are fp16 (see DsOf): the K tile is converted in place as it
+// lands, Q^T once.
+// Dropout modes of the dQ kernel.
+enum DqDrop { kDropNone = 0, kDropDraw = 1, kDropRead = 2 };
+
 template <int HS>
 struct DqCfg {
   static constexpr int NW = 4;
@@ -428,6 +434,7 @@ struct DqCfg {
   static constexpr int DB = HS / 32;
   static constexpr int NS = 3;  // LDS ring depth: tile t computes while t+1 converts and t+2 lands
   static constexpr int PER = 2 * (BN * HS / 512) / NW;  // DMA instructions per wavefront per step
+  static constexpr int KEEP_WORDS = (BM / 8) * (BN / 8) * 2;  // keep-bit tile (kDropRead), words
   static_assert((BN * HS / 512) % NW == 0, "uniform DMA split");
 };
 
@@ -444,23 +451,26 @@ enum DqTile { kFull = 0, kDiagLo = 1, kDiagHi = 2 };
 
 // `between` runs once the first block's S and dP MFMAs are issued (the ring's
 // DMA issue and tile conversion, which then overlap the matrix core's work).
-template <class E, int HS, int KIND, bool DROP, class F>
+// Bb (kDropRead): the step's keep-bit tile; kbo: this lane's byte offset in
+// it for key group 0 (query octet and byte of qrow); h: lane half.
+template <class E, int HS, int KIND, int DROP, class F>
 __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, int dn, float c,
                                         float lse2, float Dq, const LaneOffsets<HS>& L,
                                         const u32x4 (&qf)[HS / 16], const u32x4 (&gf)[HS / 16],
                                         f32x16 (&dqa)[HS / 32], f32x16 (&mka)[HS / 32],
                                         float& esum, const f32x16& negD, uint32_t qrow,
                                         uint32_t g0, uint32_t bh, const Dropout& dr,
-                                        rsrc_t rb, uint32_t ng, F&& between) {
+                                        rsrc_t rb, uint32_t ng, const uint8_t* Bb, int kbo,
+                                        int h, F&& between) {
   using C = DqCfg<HS>;
   using Ed = typename DsOf<E>::T;
   constexpr int NKB = KIND == kDiagLo ? 1 : 2;  // 32-key blocks computed
   constexpr int KD = KIND == kDiagLo ? 0 : (KIND == kDiagHi ? 1 : -1);  // the diagonal block
   u32x4 dsp[2][2], pp[2][2];
-  // Keep bits of the step's runs, drawn before the S / dP MFMAs so that the
-  // generator's vector ALU work overlaps them.
+  // Keep bits of the step's runs, drawn (and stored) before the S / dP MFMAs
+  // so that the generator's vector ALU work overlaps them, or read.
   uint32_t bits[2][2] = {{0xFFu, 0xFFu}, {0xFFu, 0xFFu}};
-  if constexpr (DROP) {
+  if constexpr (DROP == kDropDraw) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -469,6 +479,11 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
         bits[kb][t] = keep_bits8(qrow, G, bh, dr);
         if (G < ng) bstore1(rb, ((qrow >> 3) * ng + G) * 8 + (qrow & 7), bits[kb][t]);
       }
+  } else if constexpr (DROP == kDropRead) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) bits[kb][t] = Bb[kbo + 8 * (4 * kb + 2 * t + h)];
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
@@ -519,7 +534,7 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
       }
 }
 
-template <class E, int HS, bool STRIDED, bool DROP>  // STRIDED, DROP as for the dK/dV kernel
+template <class E, int HS, bool STRIDED, int DROP>  // STRIDED as for the dK/dV kernel; DqDrop
 __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) void dq16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
@@ -527,8 +542,11 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
     float* __restrict__ L2g, uint64_t* __restrict__ keep, uint16_t* __restrict__ dq, int BH,
     int H, int T, float scale, Layout li, Layout lo, Layout lg, Dropout dr) {
   using C = DqCfg<HS>;
+  constexpr bool READ = DROP == kDropRead;
+  constexpr int PER = C::PER + (READ ? 1 : 0);
   __shared__ __attribute__((aligned(16))) uint16_t Ks[C::NS][C::BN * HS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[C::NS][C::BN * HS];
+  __shared__ __attribute__((aligned(16))) uint32_t Bs[READ ? C::NS : 1][READ ? C::KEEP_WORDS : 4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
@@ -549,13 +567,26 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
   const int qrow = q0 + n;
   const int dn = n - 8 * h;
   const float c = scale * kLog2e;
-  // Keep bytes (DROP): this slice's ng x ng blocks of 8 bytes.
+  // Keep bytes (DROP): this slice's ng x ng blocks of 8 bytes.  kbo: this
+  // lane's byte in the step's keep-bit tile (16 query octets x 8 key groups
+  // of 8 bytes) for key group 0.
   const uint32_t ng = uint32_t(T + 7) >> 3;
   const rsrc_t rb = make_rsrc(DROP ? keep + int64_t(bh) * ng * ng : keep, ng * ng * 8);
+  const int kbo = ((qrow - r0) >> 3) * 64 + (qrow & 7);
 
   auto issue = [&](int kt, int buf) {
     dma_tile<HS, C::BN, C::NW>(rk, kt * C::BN, rs, Ks[buf], w, lane);
     dma_tile<HS, C::BN, C::NW>(rv, kt * C::BN, rs, Vs[buf], w, lane);
+    if constexpr (READ) {
+      // Wavefront w: query octets 4w .. 4w+3 of the workgroup, the step's 8
+      // key groups each (lane: octet 4w + lane/4, groups 2 (lane%4) and +1).
+      constexpr int KQ = C::KEEP_WORDS / C::NW;  // words per wavefront
+      const uint32_t qo = uint32_t(r0 / 8 + 4 * w + (lane >> 2));
+      if (lane < 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (__attribute__((address_space(3))) void*)(Bs[buf] + w * KQ), 16,
+            (qo * ng + uint32_t(kt * (C::BN / 8)) + 2u * uint32_t(lane & 3)) * 8, 0, 0, 0);
+    }
   };
   const int nkt = (min(r0 + C::BM, T) - 1) / C::BN + 1;
   issue(0, 0);
@@ -597,7 +628,7 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
   // Tile 0 and this wavefront's q, dO, O, lse rows (tile 1's DMA, issued
   // last, may still be in flight).
   if (1 < nkt)
-    wait_vmem_n<C::PER>();
+    wait_vmem_n<PER>();
   else
     wait_vmem();
   if constexpr (DsOf<E>::kConvert) dma_tile_to_f16<HS, C::BN, C::NW>(Ks[0], w, lane);
@@ -621,13 +652,19 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
     if (q0 < T && key0 <= q0) {
       if (key0 == q0)
         dq_step<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
-                                      negD, uq, g0, ub, dr, rb, ng, between);
+                                      negD, uq, g0, ub, dr, rb, ng,
+                                      reinterpret_cast<const uint8_t*>(Bs[READ ? buf : 0]), kbo, h,
+                                      between);
       else if (key0 + 32 == q0)
         dq_step<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
-                                      negD, uq, g0, ub, dr, rb, ng, between);
+                                      negD, uq, g0, ub, dr, rb, ng,
+                                      reinterpret_cast<const uint8_t*>(Bs[READ ? buf : 0]), kbo, h,
+                                      between);
       else
         dq_step<E, HS, kFull, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
-                                    negD, uq, g0, ub, dr, rb, ng, between);
+                                    negD, uq, g0, ub, dr, rb, ng,
+                                      reinterpret_cast<const uint8_t*>(Bs[READ ? buf : 0]), kbo, h,
+                                      between);
     } else {
       between();
     }
@@ -691,18 +728,20 @@ hipError_t dkdv16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v
 template <class E>
 hipError_t dq16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                       float* L2, uint64_t* keep, uint16_t* dq, int BH, int H, int T, int hs,
-                       float scale, Layout li, Layout lo, Layout lg, const Dropout& dr,
-                       hipStream_t s) {
+                       float* L2, uint64_t* keep, bool keep_stored, uint16_t* dq, int BH, int H,
+                       int T, int hs, float scale, Layout li, Layout lo, Layout lg,
+                       const Dropout& dr, hipStream_t s) {
   const int bm = DqCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
   auto pick = [&](auto dropc) {
-    constexpr bool D = decltype(dropc)::value;
+    constexpr int D = decltype(dropc)::value;
     return hs == 64 ? (strided ? dq16_kernel<E, 64, true, D> : dq16_kernel<E, 64, false, D>)
                     : (strided ? dq16_kernel<E, 32, true, D> : dq16_kernel<E, 32, false, D>);
   };
-  auto kern = dr.thr != 0 ? pick(std::true_type{}) : pick(std::false_type{});
+  auto kern = dr.thr == 0   ? pick(std::integral_constant<int, kDropNone>{})
+              : keep_stored ? pick(std::integral_constant<int, kDropRead>{})
+                            : pick(std::integral_constant<int, kDropDraw>{});
   return launch(kern, grid, dim3(kThreads), s, q, k, v, o, dO, lse, D, L2, keep, dq, BH, H, T,
                 scale, li, lo, lg, dr);
 }
@@ -729,14 +768,14 @@ hipError_t h16_bwd_dkdv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 hipError_t h16_bwd_dq(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const uint16_t* o, const uint16_t* dO, const float* lse, float* D,
-                      float* L2, uint64_t* keep, uint16_t* dq, int BH, int H, int T, int hs,
-                      float scale, Layout li, Layout lo, Layout lg, const Dropout& dr, bool f16,
-                      hipStream_t s) {
+                      float* L2, uint64_t* keep, bool keep_stored, uint16_t* dq, int BH, int H,
+                      int T, int hs, float scale, Layout li, Layout lo, Layout lg,
+                      const Dropout& dr, bool f16, hipStream_t s) {
   if (f16)
-    return dq16_launch<F16>(q, k, v, o, dO, lse, D, L2, keep, dq, BH, H, T, hs, scale, li, lo, lg,
-                            dr, s);
-  return dq16_launch<Bf16>(q, k, v, o, dO, lse, D, L2, keep, dq, BH, H, T, hs, scale, li, lo, lg,
-                           dr, s);
+    return dq16_launch<F16>(q, k, v, o, dO, lse, D, L2, keep, keep_stored, dq, BH, H, T, hs, scale,
+                            li, lo, lg, dr, s);
+  return dq16_launch<Bf16>(q, k, v, o, dO, lse, D, L2, keep, keep_stored, dq, BH, H, T, hs, scale,
+                           li, lo, lg, dr, s);
 }
 
 }  // namespace gattn

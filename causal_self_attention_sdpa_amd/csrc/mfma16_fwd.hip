@@ -31,7 +31,11 @@
 // based generator of philox.h: the lane's run of 8 consecutive keys of one
 // query is exactly one generator block.  The row sum l takes the weights
 // before dropout (the softmax is normalised first), the value sum only the
-// kept ones, and the output is multiplied by 1/(1 - p) with 1/l.
+// kept ones, and the output is multiplied by 1/(1 - p) with 1/l.  If the
+// caller gives a keep buffer, each run's 8 decisions are also stored there as
+// one byte of the 8x8 keep-bit blocks the backward kernels read (block (query
+// octet I, key group G) at bytes (I * ng + G) * 8 of the slice's part, byte e
+// = query 8I + e, bit r = key 8G + r, ng = ceil(T / 8)).
 // Tensors are addressed through Layout strides (q, k, v: li; o: lo), so the
 // fused (B, T, 3C) projection output and a (B, T, C) output are read and
 // written in place.  Rows past T are read as zeros (buffer resources sized to
@@ -122,9 +126,26 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb,
                                          float c, const LaneOffsets<HS>& L,
                                          const u32x4 (&qf)[HS / 16], FwdState<HS>& st,
                                          uint32_t qrow, uint32_t g0, uint32_t bh,
-                                         const Dropout& dr) {
+                                         const Dropout& dr, bool store, rsrc_t rb, uint32_t ng) {
   using C = FwdCfg<HS>;
   constexpr int NKH = KIND == kDiagLo ? 1 : 2;  // 32-key halves computed
+  // Keep bits, drawn (and stored) before the S MFMAs: the generator's vector
+  // ALU work overlaps them, and the stores have the tile to complete.
+  uint32_t bits[2][2] = {{0xFFu, 0xFFu}, {0xFFu, 0xFFu}};
+  if constexpr (DROP) {
+#pragma unroll
+    for (int kh = 0; kh < NKH; ++kh)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) bits[kh][t] = keep_bits8(qrow, g0 + 4 * kh + 2 * t, bh, dr);
+    if (store)
+#pragma unroll
+      for (int kh = 0; kh < NKH; ++kh)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t G = g0 + 4 * kh + 2 * t;
+          if (G < ng) bstore1(rb, ((qrow >> 3) * ng + G) * 8 + (qrow & 7), bits[kh][t]);
+        }
+  }
   f32x16 s[2];
 #pragma unroll
   for (int kh = 0; kh < NKH; ++kh) {
@@ -140,12 +161,6 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* Kb, const uint16_t* Vb,
     for (int i = 0; i < 16; ++i)
       if (16 * (i >> 3) + (i & 7) > dn) s[kd][i] = -INFINITY;
   }
-  uint32_t bits[2][2] = {{0xFFu, 0xFFu}, {0xFFu, 0xFFu}};
-  if constexpr (DROP)
-#pragma unroll
-    for (int kh = 0; kh < NKH; ++kh)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) bits[kh][t] = keep_bits8(qrow, g0 + 4 * kh + 2 * t, bh, dr);
   u32x4 pf[2][2];
   float ls = half_weights<E, DROP>(s[0], c, st.m * c, bits[0], pf[0]);
   if constexpr (NKH == 2) ls += half_weights<E, DROP>(s[1], c, st.m * c, bits[1], pf[1]);
@@ -185,8 +200,9 @@ __global__ __launch_bounds__(kThreads) void fwd16_kernel(const uint16_t* __restr
                                                            const uint16_t* __restrict__ k,
                                                            const uint16_t* __restrict__ v,
                                                            uint16_t* __restrict__ o,
-                                                           float* __restrict__ lse, int BH, int H,
-                                                           int T, float scale, Layout li,
+                                                           float* __restrict__ lse,
+                                                           uint64_t* __restrict__ keep, int BH,
+                                                           int H, int T, float scale, Layout li,
                                                            Layout lo, Dropout dr) {
   using C = FwdCfg<HS>;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[C::NS][C::BN * HS];
@@ -209,6 +225,10 @@ __global__ __launch_bounds__(kThreads) void fwd16_kernel(const uint16_t* __restr
   const int qrow = q0 + n;
   const int nkt = (min(r0 + C::BM, T) - 1) / C::BN + 1;
   const float c = scale * kLog2e;
+  // Keep bytes (DROP with a keep buffer): this slice's ng x ng blocks.
+  const uint32_t ng = uint32_t(T + 7) >> 3;
+  const bool store = DROP && keep != nullptr;
+  const rsrc_t rb = make_rsrc(store ? keep + int64_t(bh) * ng * ng : keep, store ? ng * ng * 8 : 0);
 
   auto issue = [&](int kt, int buf) {
     dma_tile<HS, C::BN, C::NW>(rk, kt * C::BN, rs, Ks[buf], w, lane);
@@ -243,11 +263,14 @@ __global__ __launch_bounds__(kThreads) void fwd16_kernel(const uint16_t* __restr
     const uint32_t g0 = uint32_t(key0 / 8 + h);
     if (q0 < T && key0 <= q0) {  // this wavefront sees some key of the tile
       if (key0 == q0)
-        fwd_tile<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], n, dn, c, L, qf, st, qrow, g0, bh, dr);
+        fwd_tile<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], n, dn, c, L, qf, st, qrow, g0, bh, dr,
+                                         store, rb, ng);
       else if (key0 + 32 == q0)
-        fwd_tile<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], n, dn, c, L, qf, st, qrow, g0, bh, dr);
+        fwd_tile<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], n, dn, c, L, qf, st, qrow, g0, bh, dr,
+                                         store, rb, ng);
       else
-        fwd_tile<E, HS, kFull, DROP>(Ks[buf], Vs[buf], n, dn, c, L, qf, st, qrow, g0, bh, dr);
+        fwd_tile<E, HS, kFull, DROP>(Ks[buf], Vs[buf], n, dn, c, L, qf, st, qrow, g0, bh, dr,
+                                         store, rb, ng);
     }
     wait_ring<C::NS, C::PER>(max(0, min(C::NS - 2, nkt - kt - 2)));
     __syncthreads();
@@ -280,8 +303,8 @@ __global__ __launch_bounds__(kThreads) void fwd16_kernel(const uint16_t* __restr
 namespace {
 template <class E>
 hipError_t fwd16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                        float* lse, int BH, int H, int T, int hs, float scale, Layout li,
-                        Layout lo, const Dropout& dr, hipStream_t s) {
+                        float* lse, uint64_t* keep, int BH, int H, int T, int hs, float scale,
+                        Layout li, Layout lo, const Dropout& dr, hipStream_t s) {
   const int bm = FwdCfg<64>::BM;
   const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lo);
@@ -291,15 +314,16 @@ hipError_t fwd16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     : (strided ? fwd16_kernel<E, 32, true, D> : fwd16_kernel<E, 32, false, D>);
   };
   auto kern = dr.thr != 0 ? pick(std::true_type{}) : pick(std::false_type{});
-  return launch(kern, grid, dim3(kThreads), s, q, k, v, o, lse, BH, H, T, scale, li, lo, dr);
+  return launch(kern, grid, dim3(kThreads), s, q, k, v, o, lse, dr.thr != 0 ? keep : nullptr, BH,
+                H, T, scale, li, lo, dr);
 }
 }  // namespace
 
 hipError_t h16_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                   float* lse, int BH, int H, int T, int hs, float scale, Layout li, Layout lo,
-                   const Dropout& dr, bool f16, hipStream_t s) {
-  if (f16) return fwd16_launch<F16>(q, k, v, o, lse, BH, H, T, hs, scale, li, lo, dr, s);
-  return fwd16_launch<Bf16>(q, k, v, o, lse, BH, H, T, hs, scale, li, lo, dr, s);
+                   float* lse, uint64_t* keep, int BH, int H, int T, int hs, float scale,
+                   Layout li, Layout lo, const Dropout& dr, bool f16, hipStream_t s) {
+  if (f16) return fwd16_launch<F16>(q, k, v, o, lse, keep, BH, H, T, hs, scale, li, lo, dr, s);
+  return fwd16_launch<Bf16>(q, k, v, o, lse, keep, BH, H, T, hs, scale, li, lo, dr, s);
 }
 
 }  // namespace gattn

@@ -262,44 +262,67 @@ int gattn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dO, 
  * (low half first) of word (j & 7) >> 1, and keep(i, j) = u(i, j) >= t.  The
  * same (seed, offset) draws the same mask in the forward, the backward and
  * gattn_dropout_mask; give each layer and step its own (seed, offset).
- * The forward draws the mask as it goes and stores none of it; the 16-bit
- * backward draws it once (in its dQ pass) and keeps it as bits in the
- * workspace for its dK/dV pass.
+ * The 16-bit kernels draw each decision once per training step when the
+ * caller keeps them: the forward stores the decisions it draws as bits in a
+ * keep buffer (like lse, saved for the backward), and the backward reads
+ * them.  Without a keep buffer the backward draws them once itself (in its
+ * dQ pass) and keeps them in its workspace for its dK/dV pass.  The float32
+ * path always draws them where needed.  Either way the decisions, and so the
+ * results, are the same.
  *
+ * Keep buffer layout (bf16 and fp16): per (b, h) slice, ng x ng blocks of 8
+ * bytes, ng = ceil(T / 8); block (I, G) at byte (((b*H + h) * ng + I) * ng + G)
+ * * 8 holds the decisions of queries 8I .. 8I+7 (byte e: query 8I + e) and
+ * keys 8G .. 8G+7 (bit r: key 8G + r, 1 = kept).  Only blocks with some key
+ * <= some query are written.
+ *
+ * gattn_dropout_keep_bytes: size of the keep buffer, B*H*ng*ng*8 rounded up
+ * to 256; 0 for B, H or T < 1, T > 131064, or more than 2^40 bytes.
+ */
+size_t gattn_dropout_keep_bytes(int B, int H, int T);
+
+/*
  * gattn_fwd_dropout: as gattn_fwd_strided (strides NULL = contiguous) with
  * dropout of probability p.  p = 0 (t = 0) runs exactly gattn_fwd_strided.
- * INVALID_ARG also for p not finite, p < 0, p >= 1, or t > 65535.
+ * keep: NULL, or a device buffer of gattn_dropout_keep_bytes() bytes, 16-byte
+ * aligned, into which the bf16 and fp16 kernels store the keep decisions
+ * (layout above; nothing is written for float32 or t = 0).
+ * INVALID_ARG also for p not finite, p < 0, p >= 1, or t > 65535, and for a
+ * keep buffer that is misaligned or whose shape has no keep size.
  */
 int gattn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int H, int T, int hs, float scale, int dtype, float p,
-                      uint64_t seed, uint32_t offset, const int64_t* qkv_strides,
+                      uint64_t seed, uint32_t offset, void* keep, const int64_t* qkv_strides,
                       const int64_t* o_strides, hipStream_t stream);
 
 /*
  * gattn_bwd_dropout_workspace_bytes: workspace bytes gattn_bwd_dropout needs
- * for this shape and p: gattn_bwd_workspace_bytes() plus, for bf16 and fp16
- * with p rounding to a nonzero threshold, B*H*ceil(T/8)^2*8 bytes (one bit
- * per query-key pair of each (b, h) slice, 256-byte rounded).  0 for
- * arguments gattn_bwd_dropout rejects as INVALID_ARG or UNSUPPORTED (bad
- * shape or p; 16-bit with dropout and T > 131064).
+ * without a keep buffer for this shape and p: gattn_bwd_workspace_bytes()
+ * plus, for bf16 and fp16 with p rounding to a nonzero threshold,
+ * gattn_dropout_keep_bytes() (the backward keeps the decisions it draws
+ * there).  0 for arguments gattn_bwd_dropout rejects as INVALID_ARG or
+ * UNSUPPORTED (bad shape or p; 16-bit with dropout and T > 131064).
  */
 size_t gattn_bwd_dropout_workspace_bytes(int B, int H, int T, int hs, int dtype, float p);
 
 /*
  * gattn_bwd_dropout: the backward of gattn_fwd_dropout with the same p, seed
  * and offset (o and lse as that forward wrote them); arguments and strides
- * as gattn_bwd_strided; workspace: at least
- * gattn_bwd_dropout_workspace_bytes() bytes, 256-byte aligned (contents need
- * no initialisation; GATTN_ERR_WORKSPACE if smaller).  p = 0 runs exactly
- * gattn_bwd_strided.  INVALID_ARG also for p as in gattn_fwd_dropout and,
- * for bf16 and fp16 with dropout, T > 131064.
+ * as gattn_bwd_strided.  keep: NULL, or the keep buffer that forward filled
+ * (same shape, p, seed and offset; read only, bf16 and fp16; ignored for
+ * float32 and t = 0).  workspace: 256-byte aligned, contents need no
+ * initialisation, at least gattn_bwd_workspace_bytes() bytes with a keep
+ * buffer and gattn_bwd_dropout_workspace_bytes() bytes without
+ * (GATTN_ERR_WORKSPACE if smaller).  p = 0 runs exactly gattn_bwd_strided.
+ * INVALID_ARG also for p as in gattn_fwd_dropout, a misaligned keep buffer
+ * and, for bf16 and fp16 with dropout, T > 131064.
  */
 int gattn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dO,
                       const float* lse, void* dq, void* dk, void* dv, int B, int H, int T, int hs,
                       float scale, int dtype, float p, uint64_t seed, uint32_t offset,
-                      void* workspace, size_t workspace_bytes, const int64_t* qkv_strides,
-                      const int64_t* o_strides, const int64_t* grad_strides,
-                      hipStream_t stream);
+                      const void* keep, void* workspace, size_t workspace_bytes,
+                      const int64_t* qkv_strides, const int64_t* o_strides,
+                      const int64_t* grad_strides, hipStream_t stream);
 
 /*
  * gattn_dropout_mask: the keep decisions of the mask above as bytes

@@ -217,13 +217,13 @@ def test_decode_validation(lib):
 
 
 def test_dropout_validation(lib):
-    def fwd(p=0.1, q=P, o=P, lse=P, hs=64, dtype=1, sqkv=None, so=None):
-        return lib.gattn_fwd_dropout(q, P, P, o, lse, 2, 3, 100, hs, 0.125, dtype, p, 7, 1, sqkv,
-                                     so, None)
+    def fwd(p=0.1, q=P, o=P, lse=P, hs=64, dtype=1, sqkv=None, so=None, keep=None, T=100):
+        return lib.gattn_fwd_dropout(q, P, P, o, lse, 2, 3, T, hs, 0.125, dtype, p, 7, 1, keep,
+                                     sqkv, so, None)
 
-    def bwd(p=0.1, lse=P, ws=P, wsb=1 << 20, dtype=1, sg=None):
+    def bwd(p=0.1, lse=P, ws=P, wsb=1 << 20, dtype=1, sg=None, keep=None):
         return lib.gattn_bwd_dropout(P, P, P, P, P, lse, P, P, P, 2, 3, 100, 64, 0.125, dtype, p, 7,
-                                     1, ws, wsb, None, None, sg, None)
+                                     1, keep, ws, wsb, None, None, sg, None)
 
     def mask(keep=P, B=2, H=3, T=100, p=0.1):
         return lib.gattn_dropout_mask(keep, B, H, T, p, 7, 1, None)
@@ -245,7 +245,12 @@ def test_dropout_validation(lib):
     assert bwd(wsb=ga.gattn_bwd_dropout_workspace_bytes(2, 3, 100, 64, ga.BF16, 0.1) - 1) == WORKSPACE
     big_t = 8 * 16383 + 1   # ceil(T / 8) past the keep-bit addressing limit
     assert lib.gattn_bwd_dropout(P, P, P, P, P, P, P, P, P, 1, 1, big_t, 64, 0.125, 1, 0.1, 7, 1,
-                                 P, 1 << 40, None, None, None, None) == INVALID
+                                 None, P, 1 << 40, None, None, None, None) == INVALID
+    # A keep buffer must be 16-byte aligned and its shape must have a keep size.
+    assert fwd(keep=P + 8) == INVALID
+    assert bwd(keep=P + 8) == INVALID
+    assert fwd(keep=P, T=big_t) == INVALID
+    assert fwd(keep=P, p=1.0) == INVALID
     assert bwd(sg=_st(-1, 64, 64)) == INVALID
     assert mask(keep=None) == INVALID
     assert mask(T=0) == INVALID
@@ -273,6 +278,18 @@ def test_dropout_workspace_bytes(lib):
     assert need(B=1, H=1, T=8 * 16383) > 0
     assert need(B=1, H=1, T=8 * 16383 + 1) == 0
     assert need(B=1, H=1, T=8 * 16383 + 1, dt=ga.F32) > 0
+
+
+def test_dropout_keep_bytes(lib):
+    """The keep buffer: ceil(T/8)^2 blocks of 8 bytes per (b, h), 256-byte
+    rounded, for any dtype; 0 past the addressing limit."""
+    assert ga.gattn_dropout_keep_bytes(2, 3, 100) == -(-(2 * 3 * 13 * 13 * 8) // 256) * 256
+    assert ga.gattn_dropout_keep_bytes(12, 12, 1024) == 12 * 12 * 128 * 128 * 8
+    assert ga.gattn_dropout_keep_bytes(1, 1, 1) == 256
+    assert ga.gattn_dropout_keep_bytes(0, 1, 8) == 0 and ga.gattn_dropout_keep_bytes(1, 1, 0) == 0
+    assert ga.gattn_dropout_keep_bytes(1, 1, 8 * 16383) > 0
+    assert ga.gattn_dropout_keep_bytes(1, 1, 8 * 16383 + 1) == 0
+    assert ga.gattn_dropout_keep_bytes(1 << 20, 1 << 10, 1024) == 0   # past 2^40 bytes
 
 
 def test_probe_validation(lib):

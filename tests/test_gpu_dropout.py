@@ -32,14 +32,21 @@ def _gpu():
     ga.load_library()
 
 
-def _gpu_run(x, dtype, s, p, seed, off):
-    """gattn_fwd_dropout then gattn_bwd_dropout; float64 (dq, dk, dv, o, lse)."""
+def _gpu_run(x, dtype, s, p, seed, off, stored=False):
+    """gattn_fwd_dropout then gattn_bwd_dropout; float64 (dq, dk, dv, o, lse).
+    stored: the forward stores its keep decisions and the backward reads them
+    (else the backward draws them itself)."""
     import torch
     import causal_self_attention_sdpa_amd as ga
     t = {n: to_dev(a, dtype) for n, a in x.items()}
-    o, lse = ga.attention_forward_dropout(t["q"], t["k"], t["v"], p, seed, off, scale=s)
+    keep = None
+    if stored:
+        o, lse, keep = ga.attention_forward_dropout(t["q"], t["k"], t["v"], p, seed, off, scale=s,
+                                                    return_keep=True)
+    else:
+        o, lse = ga.attention_forward_dropout(t["q"], t["k"], t["v"], p, seed, off, scale=s)
     dq, dk, dv = ga.attention_backward_dropout(t["q"], t["k"], t["v"], o, t["do"], lse, p, seed,
-                                               off, scale=s)
+                                               off, scale=s, keep=keep)
     torch.cuda.synchronize()
     return tuple(a.float().cpu().numpy().astype(np.float64) for a in (dq, dk, dv, o, lse))
 
@@ -178,14 +185,17 @@ def _grad_setup(B, H, T, hs, which, win):
     return dict(q=np.zeros_like(x["q"]), k=x["k"], v=x["v"], do=oh)
 
 
+@pytest.mark.parametrize("stored", [False, True], ids=["drawn", "stored"])
 @pytest.mark.parametrize("which", ["dq", "dk", "dv"])
 @pytest.mark.parametrize("T,win", [(300, 0), (300, 236), (1024, 960)])
-def test_backward_keep_decisions_exact(which, T, win):
+def test_backward_keep_decisions_exact(which, T, win, stored):
+    """stored: the decisions the backward uses come from the forward's keep
+    buffer instead of its own draw."""
     from oracle import dropout as od
     B, H, hs, p, seed, off, s = 2, 3, 64, 0.3, 91, 5, 0.125
     x = _grad_setup(B, H, T, hs, which, win)
-    print(f"case dropout keep read-out {which} T={T} win={win}", flush=True)
-    dq, dk, dv, o, lse = _gpu_run(x, "bf16", s, p, seed, off)
+    print(f"case dropout keep read-out {which} T={T} win={win} stored={stored}", flush=True)
+    dq, dk, dv, o, lse = _gpu_run(x, "bf16", s, p, seed, off, stored=stored)
     kept = _mask_ref(B, H, T, p, seed, off)
     zs = od.keep_scale(p)
     n = min(hs, T - win)
@@ -245,6 +255,70 @@ def test_same_seed_reproduces_other_offsets_differ():
         assert np.array_equal(a[n], b[n])
     assert not np.array_equal(a[3], c[3])
     assert np.array_equal(a[4], c[4])  # lse is that of the softmax before dropout
+
+
+@pytest.mark.parametrize("dtype,B,H,T,hs", [("bf16", 2, 3, 333, 64), ("f16", 1, 2, 130, 32),
+                                             ("bf16", 12, 12, 1024, 64)])
+def test_stored_keep_path_equals_drawn_path_bitwise(dtype, B, H, T, hs):
+    """The forward storing its keep decisions changes none of its outputs,
+    and the backward reading them gives exactly the gradients of the backward
+    that draws them itself."""
+    x = inputs(B, H, T, hs, dtype, seed=108, workload="dropout-stored")
+    s = default_scale(hs)
+    print(f"case stored keep {dtype} B={B} H={H} T={T} hs={hs}", flush=True)
+    drawn = _gpu_run(x, dtype, s, 0.1, 0x5EED, 3)
+    stored = _gpu_run(x, dtype, s, 0.1, 0x5EED, 3, stored=True)
+    for n, a, b in zip(("dq", "dk", "dv", "o", "lse"), drawn, stored):
+        assert np.array_equal(a, b), n
+
+
+@pytest.mark.parametrize("B,H,T,p,seed,off", [(2, 3, 203, 0.1, 5, 0), (1, 2, 64, 0.5, 2**63 + 11, 7),
+                                              (1, 1, 9, 0.3, 1, 1)])
+def test_stored_keep_bits_equal_mask_kernel(B, H, T, p, seed, off):
+    """The forward's keep buffer, unpacked by its documented layout (block
+    (I, G) of 8 bytes, byte e = query 8I + e, bit r = key 8G + r), equals the
+    mask kernel's decisions on every causal pair j <= i < T."""
+    import torch
+    import causal_self_attention_sdpa_amd as ga
+    hs = 64
+    x = inputs(B, H, T, hs, "bf16", seed=109, workload="dropout-keep-layout")
+    t = {n: to_dev(a, "bf16") for n, a in x.items()}
+    _, _, keep = ga.attention_forward_dropout(t["q"], t["k"], t["v"], p, seed, off,
+                                              return_keep=True)
+    mask = torch.empty((B, H, T, T), dtype=torch.uint8, device="cuda")
+    ga.gattn_dropout_mask(mask, B, H, T, p, seed, off)
+    torch.cuda.synchronize()
+    ng = -(-T // 8)
+    blocks = keep.cpu().numpy()[:B * H * ng * ng * 8].reshape(B, H, ng, ng, 8)  # (b, h, I, G, e)
+    bits = np.unpackbits(blocks[..., None], axis=-1, bitorder="little")          # (.., e, r)
+    full = bits.transpose(0, 1, 2, 4, 3, 5).reshape(B, H, 8 * ng, 8 * ng)[:, :, :T, :T]
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    ref = mask.cpu().numpy().astype(bool)
+    assert np.array_equal(full.astype(bool) & causal, ref & causal)
+
+
+def test_f32_leaves_keep_buffer_alone():
+    """The float32 path draws its decisions where needed: a keep buffer given
+    to its forward is not written, and its backward with that buffer equals
+    the one without."""
+    import torch
+    import causal_self_attention_sdpa_amd as ga
+    B, H, T, hs = 1, 2, 70, 16
+    x = inputs(B, H, T, hs, "f32", seed=110, workload="dropout-f32-keep")
+    t = {n: to_dev(a, "f32") for n, a in x.items()}
+    keep = torch.full((ga.gattn_dropout_keep_bytes(B, H, T),), 0xAB, dtype=torch.uint8,
+                      device="cuda")
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    ga.gattn_fwd_dropout(t["q"], t["k"], t["v"], o, lse, 0.25, 0.2, 3, 4, keep=keep)
+    a = ga.attention_backward_dropout(t["q"], t["k"], t["v"], o, t["do"], lse, 0.2, 3, 4,
+                                      scale=0.25, keep=keep)
+    b = ga.attention_backward_dropout(t["q"], t["k"], t["v"], o, t["do"], lse, 0.2, 3, 4,
+                                      scale=0.25)
+    torch.cuda.synchronize()
+    assert bool((keep == 0xAB).all())
+    for n, u, w in zip(("dq", "dk", "dv"), a, b):
+        assert torch.equal(u, w), n
 
 
 @pytest.mark.parametrize("dtype,T,hs", [("bf16", 200, 64), ("f16", 333, 32)])
