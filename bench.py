@@ -69,14 +69,14 @@ CSRC = os.path.join(ROOT, "causal_self_attention_sdpa_amd", "csrc")
 #          (B,H,T) fp32 row vector)
 KERNELS = {
     "fwd": ("fwd16_kernel<{E}, {hs}, false, false>", "mfma16_fwd.hip", 4, 4, 1),  # q k v in; o, lse out
-    "dq": ("dq16_kernel<{E}, {hs}, false, false>", "mfma16_bwd.hip", 2, 6, 1),  # q k v o dO lse in; dq out
+    "dq": ("dq16_kernel<{E}, {hs}, false, 0>", "mfma16_bwd.hip", 2, 6, 1),  # q k v o dO lse in; dq out
     "dkdv": ("dkdv16_kernel<{E}, {hs}, false, false>", "mfma16_bwd.hip", 6, 6, 0),  # q k v dO in; dk dv out
 }
 # With attention dropout (--dropout): the forward kernel, and the backward as
 # one call (its dQ and dK/dV kernels back to back), timed as one unit.
 DROP_KERNELS = {
     "fwd_dropout": ("fwd16_kernel<{E}, {hs}, false, true>", "mfma16_fwd.hip", 4, 4, 1),
-    "bwd_dropout": ("dq16_kernel<{E}, {hs}, false, true> + dkdv16_kernel<{E}, {hs}, false, true>",
+    "bwd_dropout": ("dq16_kernel<{E}, {hs}, false, 2> + dkdv16_kernel<{E}, {hs}, false, true>",
                     "mfma16_bwd.hip", 8, 8, 1),  # q k v o dO lse in; dq dk dv out
 }
 
