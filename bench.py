@@ -312,7 +312,8 @@ def decode_main(args) -> int:
                           "B": B, "H": H, "Tq": 1, "Tk": Tk, "hs": hs, "layers": L,
                           "parallelism": "single GPU"},
                "us_per_call": round(per_call, 2),
-               "roofline": {"kernel": "dec16_kernel + dec16_combine (one gattn_fwd_decode call)",
+               "roofline": {"kernel": "one gattn_fwd_decode call (dec1_kernel for one new token, "
+                                      "plus dec16_combine when the keys are split)",
                             "bound": "hbm", "achieved": round(alg / (per_call * 1e-6) / 1e9, 1),
                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(alg / (per_call * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -482,6 +483,8 @@ def main() -> int:
         for g in ("dq", "dk", "dv"):
             t[g] = torch.empty_like(t["q"])
         layers.append(t)
+        if B * H * T * hs >= 1 << 26:  # long sequences: report progress while generating
+            print(f"[bench] layer {l} generated", file=sys.stderr, flush=True)
     drop = args.dropout > 0.0
     ws = torch.empty(ga.gattn_bwd_workspace_bytes(B, H, T, hs, dcode), dtype=torch.uint8,
                      device=dev)
