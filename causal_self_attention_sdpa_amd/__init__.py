@@ -13,8 +13,9 @@ allocate the outputs with torch and call those; `attention_forward_qkv` /
 projection output, reading q, k, v in place and writing y (B, T, C) and the
 gradient dqkv (B, T, 3C) through the strided entry points.
 `attention_forward_dropout` / `attention_backward_dropout` add dropout on the
-attention weights (mask from a seed and an offset, recomputed in the
-backward, never stored).
+attention weights (mask from a seed and an offset; with return_keep the
+forward also returns its keep decisions as bits, which the backward then
+reads instead of drawing them again).
 """
 from ._binding import (  # noqa: F401
     BF16,

@@ -22,11 +22,13 @@
 // forward computed O = (P*Z) V, and the chain rule gives
 //   dV = (P*Z)^T dO,   dP = Z * (dO V^T),   dS = P * (dP - D)
 // with the same D = rowsum(dO * O) (sum_j P Z (dO V^T) = dO . O).  The keep
-// decisions are recomputed from each weight's position, not stored.
+// decisions come as bits: stored by the forward, or drawn once by the dQ
+// kernel from each weight's position and stored for the dK/dV kernel.
 //
-// Both kernels stream tiles into double-buffered, swizzled LDS tiles by LDS
-// DMA (no register staging) with one barrier per step: the DMA for step t+1
-// runs while step t computes.  Tensors are addressed through Layout strides
+// Both kernels stream tiles into swizzled LDS rings by LDS DMA (no register
+// staging) with one barrier per step, so the DMA of later steps runs while a
+// step computes (two stages for dK/dV, three for dQ, whose K tile is also
+// converted to fp16 one step ahead).  Tensors are addressed through Layout strides
 // (q, k, v: li; o, dO: lo; dq, dk, dv: lg), and global accesses go through
 // buffer resources sized to the span of one (b, h) slice, so rows past T read
 // as zero and their stores are dropped.  A query row past T then has zero q and dO rows (and D = lse = 0):
