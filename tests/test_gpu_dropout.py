@@ -350,9 +350,11 @@ def test_workspace_contents_do_not_matter(dtype, T, hs):
             assert torch.equal(a, b), name
 
 
-def test_fused_qkv_layout_equals_contiguous_bitwise():
+@pytest.mark.parametrize("stored", [False, True], ids=["drawn", "stored"])
+def test_fused_qkv_layout_equals_contiguous_bitwise(stored):
     """Dropout through strided (B, T, 3C) / (B, T, C) views gives the same bits
-    as the contiguous call."""
+    as the contiguous call, with the backward's keep decisions drawn or read
+    from the strided forward's keep buffer."""
     import torch
     import causal_self_attention_sdpa_amd as ga
     B, H, T, hs, p = 2, 4, 160, 64, 0.1
@@ -368,13 +370,17 @@ def test_fused_qkv_layout_equals_contiguous_bitwise():
     y = torch.empty((B, T, C), dtype=torch.bfloat16, device="cuda")
     y4 = y.view(B, T, H, hs).transpose(1, 2)
     lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
-    ga.gattn_fwd_dropout(q, k, v, y4, lse, s, p, 21, 4)
+    keep = (torch.empty(ga.gattn_dropout_keep_bytes(B, H, T), dtype=torch.uint8, device="cuda")
+            if stored else None)
+    ga.gattn_fwd_dropout(q, k, v, y4, lse, s, p, 21, 4, keep=keep)
     dqkv = torch.empty_like(qkv)
     g4 = dqkv.view(B, T, 3, H, hs)
-    ws = torch.empty(ga.gattn_bwd_dropout_workspace_bytes(B, H, T, hs, ga.BF16, p),
-                     dtype=torch.uint8, device="cuda")
+    nws = (ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16) if stored
+           else ga.gattn_bwd_dropout_workspace_bytes(B, H, T, hs, ga.BF16, p))
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
     ga.gattn_bwd_dropout(q, k, v, y4, dy.view(B, T, H, hs).transpose(1, 2), lse,
-                         *(g4[:, :, j].transpose(1, 2) for j in range(3)), s, p, 21, 4, ws)
+                         *(g4[:, :, j].transpose(1, 2) for j in range(3)), s, p, 21, 4, ws,
+                         keep=keep)
     torch.cuda.synchronize()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)
     got = (f(g4[:, :, 0].transpose(1, 2)), f(g4[:, :, 1].transpose(1, 2)),
