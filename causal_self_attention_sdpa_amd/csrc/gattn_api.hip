@@ -88,10 +88,12 @@ int dropout_of(float p, uint64_t seed, uint32_t offset, gattn::Dropout& d) {
   d.k1 = uint32_t(seed >> 32);
   d.off = offset;
   d.zs = float(65536.0 / (65536.0 - t));
+  d.izs = float((65536.0 - t) / 65536.0);
+  d.lzs = float(std::log2(65536.0 / (65536.0 - t)));
   return GATTN_OK;
 }
 
-const gattn::Dropout kNoDropout{0, 0, 0, 0, 1.f};
+const gattn::Dropout kNoDropout{0, 0, 0, 0, 1.f, 1.f, 0.f};
 
 // Workspace parts: D, then L2 = lse * log2(e).
 float* ws_D(void* ws) { return static_cast<float*>(ws); }

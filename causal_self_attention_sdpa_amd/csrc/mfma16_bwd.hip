@@ -23,7 +23,11 @@
 //   dV = (P*Z)^T dO,   dP = Z * (dO V^T),   dS = P * (dP - D)
 // with the same D = rowsum(dO * O) (sum_j P Z (dO V^T) = dO . O).  The keep
 // decisions come as bits: stored by the forward, or drawn once by the dQ
-// kernel from each weight's position and stored for the dK/dV kernel.
+// kernel from each weight's position and stored for the dK/dV kernel.  The
+// kept weights' factor zs is folded into the exponent (pz = P zs =
+// 2^(s c - (L2 - log2 zs))), so with the row terms D z = D / zs a weight's
+// dS = pz (keep ? dP - D z : -D z) and its dV weight pz keep; with dropout
+// the workspace holds L2 - log2 zs and D / zs for the dK/dV kernel.
 //
 // Both kernels stream tiles into swizzled LDS rings by LDS DMA (no register
 // staging) with one barrier per step, so the DMA of later steps runs while a
@@ -184,7 +188,7 @@ template <class E, int HS, bool MASK, bool DROP>
 __device__ __forceinline__ void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
                                  const float* Db, const uint32_t* Bb, int qb, int qs0, int krow,
                                  int h, float c, const LaneOffsets<HS>& L, const f32x16& s,
-                                 const f32x16& dp, DkdvRegs<HS>& R, int gl, float zs) {
+                                 const f32x16& dp, DkdvRegs<HS>& R, int gl) {
   using C = DkdvCfg<HS>;
   u32x4 pp[2], dsp[2];
 #pragma unroll
@@ -205,8 +209,8 @@ __device__ __forceinline__ void dkdv_grad(const uint16_t* Qb, const uint16_t* Gb
       if (MASK && krow > qs0 + ql + e) p = 0.f;
       if constexpr (DROP) {
         const uint32_t m = keep_mask(w[e >> 2], 8 * (e & 3));
-        pv[e] = __uint_as_float(__float_as_uint(p) & m);
-        dsv[e] = p * (__uint_as_float(__float_as_uint(dp[8 * t + e] * zs) & m) - De);
+        pv[e] = __uint_as_float(__float_as_uint(p) & m);  // p is P zs, De is D / zs
+        dsv[e] = p * (__uint_as_float(__float_as_uint(dp[8 * t + e]) & m) - De);
       } else {
         pv[e] = p;
         dsv[e] = p * (dp[8 * t + e] - De);
@@ -235,15 +239,14 @@ template <class E, int HS, bool DROP, bool KVL>
 __device__ __forceinline__ void dkdv_step_full(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
                                       const float* Db, const uint32_t* Bb, const uint16_t* KVb,
                                       int kl, int qs0, int krow, int h, float c,
-                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R, int gl,
-                                      float zs) {
+                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R, int gl) {
   using C = DkdvCfg<HS>;
   static_assert(C::QB == 2, "two query blocks per step");
   f32x16 s0, dp0, s1, dp1;
   dkdv_sdp<E, HS, KVL>(Qb, Gb, KVb, kl, h, 0, L, R, s0, dp0);
   dkdv_sdp<E, HS, KVL>(Qb, Gb, KVb, kl, h, 1, L, R, s1, dp1);
-  dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, Bb, 0, qs0, krow, h, c, L, s0, dp0, R, gl, zs);
-  dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, Bb, 1, qs0, krow, h, c, L, s1, dp1, R, gl, zs);
+  dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, Bb, 0, qs0, krow, h, c, L, s0, dp0, R, gl);
+  dkdv_grad<E, HS, false, DROP>(Qb, Gb, Lb, Db, Bb, 1, qs0, krow, h, c, L, s1, dp1, R, gl);
 }
 
 // A step that meets the diagonal: blocks wholly before this wavefront's keys
@@ -252,15 +255,14 @@ template <class E, int HS, bool DROP, bool KVL>
 __device__ __forceinline__ void dkdv_step_diag(const uint16_t* Qb, const uint16_t* Gb, const float* Lb,
                                       const float* Db, const uint32_t* Bb, const uint16_t* KVb,
                                       int kl, int qs0, int kw0, int krow, int h, float c,
-                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R, int gl,
-                                      float zs) {
+                                      const LaneOffsets<HS>& L, DkdvRegs<HS>& R, int gl) {
   using C = DkdvCfg<HS>;
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
     if (kw0 > qs0 + qb * 32 + 31) continue;  // all of this wavefront's keys lie after the block
     f32x16 s, dp;
     dkdv_sdp<E, HS, KVL>(Qb, Gb, KVb, kl, h, qb, L, R, s, dp);
-    dkdv_grad<E, HS, true, DROP>(Qb, Gb, Lb, Db, Bb, qb, qs0, krow, h, c, L, s, dp, R, gl, zs);
+    dkdv_grad<E, HS, true, DROP>(Qb, Gb, Lb, Db, Bb, qb, qs0, krow, h, c, L, s, dp, R, gl);
   }
 }
 
@@ -372,10 +374,10 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
     const uint32_t* Bb = Bs[DROP ? buf : 0];
     if (qs0 < k0 + C::BN)
       dkdv_step_diag<E, HS, DROP, KVL>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], Bb, KVs, krow - k0, qs0, kw0,
-                                  krow, h, c, L, R, gl, dr.zs);
+                                  krow, h, c, L, R, gl);
     else
       dkdv_step_full<E, HS, DROP, KVL>(Qs[buf], Gs[buf], Ls[buf], Ds[buf], Bb, KVs, krow - k0, qs0,
-                                  krow, h, c, L, R, gl, dr.zs);
+                                  krow, h, c, L, R, gl);
     wait_ring<C::NS, PER>(max(0, min(C::NS - 2, nsteps - t - 2)));
     if constexpr (DsOf<E>::kConvert)
       if (t + 1 < nsteps) dma_tile_to_f16<HS, C::BQ, C::NW>(Qs[(buf + 1) % C::NS], w, lane);
@@ -388,14 +390,13 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
   const uint32_t gbytes = slice_bytes_of<HS, STRIDED>(lg, T);
   const rsrc_t wk = make_rsrc(dk + gbase, gbytes), wv = make_rsrc(dv + gbase, gbytes);
   const int rsg = STRIDED ? int(lg.st) : HS;
-  const float zv = DROP ? dr.zs : 1.f;  // dV = (P*Z)^T dO: the kept weights' factor
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t off = uint32_t(krow * rsg + db * 32 + 8 * g + 4 * h) * 2;
-      bstore8(wv, off, u32x2{E::pack(R.dva[db][4 * g] * zv, R.dva[db][4 * g + 1] * zv),
-                             E::pack(R.dva[db][4 * g + 2] * zv, R.dva[db][4 * g + 3] * zv)});
+      bstore8(wv, off, u32x2{E::pack(R.dva[db][4 * g], R.dva[db][4 * g + 1]),
+                             E::pack(R.dva[db][4 * g + 2], R.dva[db][4 * g + 3])});
       bstore8(wk, off, u32x2{E::pack(R.dka[db][4 * g] * scale, R.dka[db][4 * g + 1] * scale),
                              E::pack(R.dka[db][4 * g + 2] * scale, R.dka[db][4 * g + 3] * scale)});
     }
@@ -489,9 +490,9 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
   }
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    // Without dropout the dP accumulator starts from -D~ (every register of
-    // a lane is this lane's query), so it ends as dP - D~.
-    f32x16 st = {}, dpt = DROP ? f32x16{} : negD;
+    // The dP accumulator starts from -D~ (every register of a lane is this
+    // lane's query; with dropout -D~/zs), so it ends as dP - D~ (dP - D~/zs).
+    f32x16 st = {}, dpt = negD;
 #pragma unroll
     for (int ks = 0; ks < C::KSTEP; ++ks) {
       st = Ed::mfma(op_nat<HS>(Kb, L, kb * 32, ks), qf[ks], st);
@@ -510,10 +511,13 @@ __device__ __forceinline__ void dq_step(const uint16_t* Kb, const uint16_t* Vb, 
         float p = __builtin_amdgcn_exp2f(fmaf(st[8 * t + e], c, -lse2));
         if (kb == KD && 16 * t + e > dn) p = 0.f;
         pv[e] = p;
-        if constexpr (DROP)
-          dsv[e] = p * (keep_or_zero(dpt[8 * t + e] * dr.zs, bits[kb][t], e) - Dq);
-        else
+        if constexpr (DROP) {  // p is P zs here, Dq is D~ / zs
+          const uint32_t m = keep_mask(bits[kb][t], e);
+          dsv[e] = p * __uint_as_float((__float_as_uint(dpt[8 * t + e]) & m) |
+                                       (__float_as_uint(-Dq) & ~m));
+        } else {
           dsv[e] = p * dpt[8 * t + e];
+        }
         esum += dsv[e];
       }
 #pragma unroll
@@ -613,7 +617,9 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
   const float lse2 = bloadf(make_rsrc(lse + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4) *
                      kLog2e;
   if (1 < nkt) issue(1, 1);
-  const float Dq = halves_sum(dpart);
+  // With dropout the weights come out as P zs and the row term as D~ / zs.
+  const float Dq = DROP ? halves_sum(dpart) * dr.izs : halves_sum(dpart);
+  const float lse2x = DROP ? lse2 - dr.lzs : lse2;
   if constexpr (DsOf<E>::kConvert) {
 #pragma unroll
     for (int ks = 0; ks < C::KSTEP; ++ks) qf[ks] = bf16x8_to_f16x8(qf[ks]);
@@ -653,17 +659,17 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
     const uint32_t g0 = uint32_t(key0 / 8 + h), ub = uint32_t(bh), uq = uint32_t(qrow);
     if (q0 < T && key0 <= q0) {
       if (key0 == q0)
-        dq_step<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
+        dq_step<E, HS, kDiagLo, DROP>(Ks[buf], Vs[buf], dn, c, lse2x, Dq, L, qf, gf, dqa, mka, esum,
                                       negD, uq, g0, ub, dr, rb, ng,
                                       reinterpret_cast<const uint8_t*>(Bs[READ ? buf : 0]), kbo, h,
                                       between);
       else if (key0 + 32 == q0)
-        dq_step<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
+        dq_step<E, HS, kDiagHi, DROP>(Ks[buf], Vs[buf], dn, c, lse2x, Dq, L, qf, gf, dqa, mka, esum,
                                       negD, uq, g0, ub, dr, rb, ng,
                                       reinterpret_cast<const uint8_t*>(Bs[READ ? buf : 0]), kbo, h,
                                       between);
       else
-        dq_step<E, HS, kFull, DROP>(Ks[buf], Vs[buf], dn, c, lse2, Dq, L, qf, gf, dqa, mka, esum,
+        dq_step<E, HS, kFull, DROP>(Ks[buf], Vs[buf], dn, c, lse2x, Dq, L, qf, gf, dqa, mka, esum,
                                     negD, uq, g0, ub, dr, rb, ng,
                                       reinterpret_cast<const uint8_t*>(Bs[READ ? buf : 0]), kbo, h,
                                       between);
@@ -676,15 +682,18 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
 
   // eps = D - D~ (both halves of the wavefront hold this query's keys).
   // dQ^T register i of lane (n, h): column d = db*32 + 8*(i/4) + 4h + i%4, query qrow.
+  // With dropout: eps as without (sum_j P (Z dP - D~)), Dq = D~/zs, M summed
+  // from P zs, and the workspace takes D/zs and L2 - log2 zs.
   const float eps = halves_sum(esum);
+  const float epm = DROP ? eps * dr.izs : eps;  // eps against the M accumulator
   if (h == 0) {
-    bstoref(make_rsrc(Dg + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4, Dq + eps);
-    bstoref(make_rsrc(L2g + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4, lse2);
+    bstoref(make_rsrc(Dg + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4, Dq + epm);
+    bstoref(make_rsrc(L2g + long(bh) * T, uint32_t(T) * 4), uint32_t(qrow) * 4, lse2x);
   }
   const rsrc_t wq = make_rsrc(dq + slice_base<HS, STRIDED>(lg, bh, H, T),
                               slice_bytes_of<HS, STRIDED>(lg, T));
   const int rsg = STRIDED ? int(lg.st) : HS;
-  auto fin = [&](int db, int i) { return fmaf(-eps, mka[db][i], dqa[db][i]) * scale; };
+  auto fin = [&](int db, int i) { return fmaf(-epm, mka[db][i], dqa[db][i]) * scale; };
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll

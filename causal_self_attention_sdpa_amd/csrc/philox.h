@@ -32,6 +32,8 @@ struct Dropout {
   uint32_t off;     // fourth counter word (a caller-chosen stream index)
   uint32_t thr;     // a weight is kept when its 16-bit value is >= thr
   float zs;         // 65536 / (65536 - thr): the factor on kept weights
+  float izs;        // 1 / zs = (65536 - thr) / 65536 (exact)
+  float lzs;        // log2(zs): the backward folds zs into its exponent
 };
 
 struct Philox4 {
