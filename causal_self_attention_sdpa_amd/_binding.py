@@ -35,6 +35,15 @@ def load_library():
     if not os.path.exists(_LIB_PATH):
         from . import build as _build
         _build.build()
+    # torch's HIP runtime must be in the process before libgattn.so: the library
+    # asks for libamdhip64.so.7, which then resolves to torch's copy (same
+    # soname).  Loaded the other way round, the library would bring in the
+    # system runtime and torch a second one of its own, and torch's streams and
+    # allocations would not be valid in the runtime the library launches on.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.gattn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
