@@ -127,10 +127,20 @@ def _dev(t, name: str, shape=None, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream):
+def _on(stream, *tensors):
+    """The stream a call launches on: the given one, else the current stream of
+    the device that holds the call's tensors (all of them on one device, and a
+    given stream on that device too)."""
     torch = _torch()
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError("the tensors of one call must be on one device, got "
+                         f"{sorted(map(str, devs))}")
+    dev = devs.pop()
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
+    elif stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -151,7 +161,8 @@ def gattn_fwd(q, k, v, o, lse, scale: float, stream=None) -> None:
     dt = _dtype_code(q)
     args = [_dev(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"))]
     lp = None if lse is None else _dev(lse, "lse", (B, H, T), _torch().float32)
-    _check(lib.gattn_fwd(*args, lp, B, H, T, hs, float(scale), dt, _stream(stream)), "gattn_fwd")
+    st = _on(stream, q, k, v, o, lse)
+    _check(lib.gattn_fwd(*args, lp, B, H, T, hs, float(scale), dt, st), "gattn_fwd")
 
 
 def gattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale: float, workspace, stream=None) -> None:
@@ -164,8 +175,9 @@ def gattn_bwd(q, k, v, o, dO, lse, dq, dk, dv, scale: float, workspace, stream=N
     outs = [_dev(x, n, q.shape, q.dtype) for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
     ws = _dev(workspace, "workspace")
     nbytes = workspace.numel() * workspace.element_size()
+    st = _on(stream, q, k, v, o, dO, lse, dq, dk, dv, workspace)
     _check(lib.gattn_bwd(*ptrs, lp, *outs, B, H, T, hs, float(scale), dt, ws, nbytes,
-                         _stream(stream)), "gattn_bwd")
+                         st), "gattn_bwd")
 
 
 def gattn_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, scale: float, stream=None) -> None:
@@ -177,8 +189,10 @@ def gattn_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, scale: float, stream=None
             ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"))]
     lp = _dev(lse, "lse", (B, H, T), _torch().float32)
     outs = [_dev(x, n, q.shape, q.dtype) for x, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
-    _check(lib.gattn_bwd_noalloc(*ptrs, lp, *outs, B, H, T, hs, float(scale), dt,
-                                 _stream(stream)), "gattn_bwd_noalloc")
+    st = _on(stream, q, k, v, o, dO, lse, dq, dk, dv)
+    with _torch().cuda.device(q.device):  # the scratch used is the current device's
+        _check(lib.gattn_bwd_noalloc(*ptrs, lp, *outs, B, H, T, hs, float(scale), dt, st),
+               "gattn_bwd_noalloc")
 
 
 def gattn_bwd_noalloc_max_bytes() -> int:
@@ -188,10 +202,11 @@ def gattn_bwd_noalloc_max_bytes() -> int:
 def gattn_bwd_preprocess(o, dO, lse, workspace, stream=None) -> None:
     lib = load_library()
     B, H, T, hs = _shape4(o)
+    st = _on(stream, o, dO, lse, workspace)
     _check(lib.gattn_bwd_preprocess(_dev(o, "o"), _dev(dO, "dO", o.shape, o.dtype),
                                     _dev(lse, "lse", (B, H, T), _torch().float32), B, H, T, hs,
                                     _dtype_code(o), _dev(workspace, "workspace"),
-                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+                                    workspace.numel() * workspace.element_size(), st),
            "gattn_bwd_preprocess")
 
 
@@ -201,9 +216,10 @@ def gattn_bwd_dq(q, k, v, o, dO, lse, dq, scale: float, workspace, stream=None) 
     ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in
             ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dO, "dO"))]
     lp = _dev(lse, "lse", (B, H, T), _torch().float32)
+    st = _on(stream, q, k, v, o, dO, lse, dq, workspace)
     _check(lib.gattn_bwd_dq(*ptrs, lp, _dev(dq, "dq", q.shape, q.dtype), B, H, T, hs,
                             float(scale), _dtype_code(q), _dev(workspace, "workspace"),
-                            workspace.numel() * workspace.element_size(), _stream(stream)),
+                            workspace.numel() * workspace.element_size(), st),
            "gattn_bwd_dq")
 
 
@@ -212,9 +228,10 @@ def gattn_bwd_dkdv(q, k, v, dO, dk, dv, scale: float, workspace, stream=None) ->
     B, H, T, hs = _shape4(q)
     ptrs = [_dev(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO"))]
     outs = [_dev(x, n, q.shape, q.dtype) for x, n in ((dk, "dk"), (dv, "dv"))]
+    st = _on(stream, q, k, v, dO, dk, dv, workspace)
     _check(lib.gattn_bwd_dkdv(*ptrs, *outs, B, H, T, hs, float(scale), _dtype_code(q),
                               _dev(workspace, "workspace"),
-                              workspace.numel() * workspace.element_size(), _stream(stream)),
+                              workspace.numel() * workspace.element_size(), st),
            "gattn_bwd_dkdv")
 
 
@@ -248,9 +265,10 @@ def gattn_fwd_strided(q, k, v, o, lse, scale: float, stream=None) -> None:
     qkv = [_view(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
     ov = _view(o, "o", q.shape, q.dtype)
     lp = None if lse is None else _dev(lse, "lse", (B, H, T), _torch().float32)
+    st = _on(stream, q, k, v, o, lse)
     _check(lib.gattn_fwd_strided(*(p for p, _ in qkv), ov[0], lp, B, H, T, hs, float(scale), dt,
                                  _strides_arg(qkv, "q, k, v"), _strides_arg([ov], "o"),
-                                 _stream(stream)), "gattn_fwd_strided")
+                                 st), "gattn_fwd_strided")
 
 
 def gattn_bwd_strided(q, k, v, o, dO, lse, dq, dk, dv, scale: float, workspace,
@@ -266,10 +284,11 @@ def gattn_bwd_strided(q, k, v, o, dO, lse, dq, dk, dv, scale: float, workspace,
     lp = _dev(lse, "lse", (B, H, T), _torch().float32)
     ws = _dev(workspace, "workspace")
     nbytes = workspace.numel() * workspace.element_size()
+    st = _on(stream, q, k, v, o, dO, lse, dq, dk, dv, workspace)
     _check(lib.gattn_bwd_strided(*(p for p, _ in qkv), *(p for p, _ in od), lp,
                                  *(p for p, _ in gr), B, H, T, hs, float(scale), dt, ws, nbytes,
                                  _strides_arg(qkv, "q, k, v"), _strides_arg(od, "o, dO"),
-                                 _strides_arg(gr, "dq, dk, dv"), _stream(stream)),
+                                 _strides_arg(gr, "dq, dk, dv"), st),
            "gattn_bwd_strided")
 
 
@@ -297,10 +316,11 @@ def gattn_fwd_decode(q, k, v, o, lse, scale: float, workspace=None, stream=None)
         workspace = _torch().empty(need, dtype=_torch().uint8, device=q.device)
     ws = None if workspace is None else _dev(workspace, "workspace")
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _on(stream, q, k, v, o, lse, workspace)
     _check(lib.gattn_fwd_decode(qv[0], kvv[0][0], kvv[1][0], ov[0], lp, B, H, Tq, Tk, hs,
                                 float(scale), dt, _strides_arg([qv], "q"),
                                 _strides_arg(kvv, "k, v"), _strides_arg([ov], "o"), ws, nbytes,
-                                _stream(stream)), "gattn_fwd_decode")
+                                st), "gattn_fwd_decode")
 
 
 def attention_decode(q, k, v, scale=None, need_lse: bool = False, workspace=None, stream=None):
@@ -339,10 +359,11 @@ def gattn_fwd_dropout(q, k, v, o, lse, scale: float, p: float, seed: int, offset
     qkv = [_view(x, n, q.shape, q.dtype) for x, n in ((q, "q"), (k, "k"), (v, "v"))]
     ov = _view(o, "o", q.shape, q.dtype)
     lp = None if lse is None else _dev(lse, "lse", (B, H, T), _torch().float32)
+    st = _on(stream, q, k, v, o, lse, keep)
     _check(lib.gattn_fwd_dropout(*(x for x, _ in qkv), ov[0], lp, B, H, T, hs, float(scale), dt,
                                  float(p), int(seed), int(offset), _keep_arg(keep, B, H, T),
                                  _strides_arg(qkv, "q, k, v"), _strides_arg([ov], "o"),
-                                 _stream(stream)), "gattn_fwd_dropout")
+                                 st), "gattn_fwd_dropout")
 
 
 def gattn_bwd_dropout_workspace_bytes(B: int, H: int, T: int, hs: int, dtype: int,
@@ -363,11 +384,12 @@ def gattn_bwd_dropout(q, k, v, o, dO, lse, dq, dk, dv, scale: float, p: float, s
     lp = _dev(lse, "lse", (B, H, T), _torch().float32)
     ws = _dev(workspace, "workspace")
     nbytes = workspace.numel() * workspace.element_size()
+    st = _on(stream, q, k, v, o, dO, lse, dq, dk, dv, workspace, keep)
     _check(lib.gattn_bwd_dropout(*(x for x, _ in qkv), *(x for x, _ in od), lp,
                                  *(x for x, _ in gr), B, H, T, hs, float(scale), dt, float(p),
                                  int(seed), int(offset), _keep_arg(keep, B, H, T), ws, nbytes,
                                  _strides_arg(qkv, "q, k, v"), _strides_arg(od, "o, dO"),
-                                 _strides_arg(gr, "dq, dk, dv"), _stream(stream)),
+                                 _strides_arg(gr, "dq, dk, dv"), st),
            "gattn_bwd_dropout")
 
 
@@ -376,8 +398,9 @@ def gattn_dropout_mask(keep, B: int, H: int, T: int, p: float, seed: int, offset
     """Writes the keep decisions (uint8, 1 = kept) into keep (B, H, T, T)."""
     torch = _torch()
     kp = _dev(keep, "keep", (B, H, T, T), torch.uint8)
+    st = _on(stream, keep)
     _check(load_library().gattn_dropout_mask(kp, B, H, T, float(p), int(seed), int(offset),
-                                             _stream(stream)), "gattn_dropout_mask")
+                                             st), "gattn_dropout_mask")
 
 
 def attention_forward_dropout(q, k, v, p: float, seed: int, offset: int = 0, scale=None,

@@ -341,3 +341,20 @@ def test_contiguous_16bit_slice_byte_limit(lib):
         assert _fwd(lib, T=2 * limit + 256, hs=32, dtype=dt) == INVALID
     # float32 addresses rows with 64-bit offsets: only B*H*T*hs < 2^31 applies
     assert ga.gattn_bwd_workspace_bytes(1, 1, limit, 64, ga.F32) > 0
+
+
+def test_binding_keeps_a_call_on_one_device():
+    """The binding's stream choice: tensors of one call on two devices, or a
+    stream of another device, are rejected before anything reaches the
+    library (stand-ins carrying only a device, so no GPU is touched)."""
+    import types
+    import torch
+    from causal_self_attention_sdpa_amd import _binding as b
+    t0 = types.SimpleNamespace(device=torch.device("cuda", 0))
+    t1 = types.SimpleNamespace(device=torch.device("cuda", 1))
+    with pytest.raises(ValueError, match="one device"):
+        b._on(None, t0, t1)
+    s1 = types.SimpleNamespace(device=torch.device("cuda", 1), cuda_stream=1234)
+    with pytest.raises(ValueError, match="stream is on"):
+        b._on(s1, t0, None, t0)
+    assert b._on(s1, t1, None).value == 1234
