@@ -5,7 +5,8 @@ allocation, no memset, no host synchronisation), so a caller can capture a
 forward and backward (and a decode step) once and replay them.  The graph is
 replayed several times with the program's own eager work and synchronisations
 in between, and every replay must give the same bits as the eager calls on the
-same inputs.
+same inputs.  Calls given an explicit stream (not the current one) give the
+same bits as on the current stream.
 """
 import numpy as np
 import pytest
@@ -99,3 +100,34 @@ def test_decode_step_graph_replays_equal_eager():
         ga.gattn_fwd_decode(q, k, v, o, lse, s, ws)
         torch.cuda.synchronize()
         assert torch.equal(got_o, o) and torch.equal(got_l, lse), f"replay {r}"
+
+
+def test_explicit_stream_argument_equals_default_stream():
+    """The calls given a stream of their own (not the current one) enqueue there
+    and give the same bits as on the current stream."""
+    import torch
+    import causal_self_attention_sdpa_amd as ga
+    B, H, T, hs = 2, 3, 150, 64
+    x = inputs(B, H, T, hs, "bf16", seed=113, workload="stream")
+    s = default_scale(hs)
+    print(f"case explicit stream bf16 B={B} H={H} T={T} hs={hs}", flush=True)
+    t = {n: to_dev(a, "bf16") for n, a in x.items()}
+
+    def run(stream):
+        o, lse = ga.attention_forward(t["q"], t["k"], t["v"], s, stream=stream)
+        dq, dk, dv = ga.attention_backward(t["q"], t["k"], t["v"], o, t["do"], lse, s,
+                                           stream=stream)
+        od, ld, keep = ga.attention_forward_dropout(t["q"], t["k"], t["v"], 0.1, 7, 1, s,
+                                                    stream=stream, return_keep=True)
+        gd = ga.attention_backward_dropout(t["q"], t["k"], t["v"], od, t["do"], ld, 0.1, 7, 1, s,
+                                           stream=stream, keep=keep)
+        return (o, lse, dq, dk, dv, od, ld, *gd)
+
+    ref = run(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = run(side)
+    side.synchronize()
+    for i, (a, b) in enumerate(zip(got, ref)):
+        assert torch.equal(a, b), i
