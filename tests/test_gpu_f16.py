@@ -71,7 +71,7 @@ def test_f16_more_accurate_than_bf16():
         sl = [(0, 0), (1, 3)]
         got = pick(gpu_fwd_bwd(x, dt, s), sl)
         ref = oracle_slices(x, s, sl)
-        errs[dt] = max(float(np.max(np.abs(g - r))) for g, r in zip(got[:4], ref[:4]))
+        errs[dt] = float(np.max([np.max(np.abs(g - r)) for g, r in zip(got[:4], ref[:4])]))
     print(f"max abs error bf16 {errs['bf16']:.3g} f16 {errs['f16']:.3g}", flush=True)
     assert errs["f16"] < errs["bf16"] / 3
 
