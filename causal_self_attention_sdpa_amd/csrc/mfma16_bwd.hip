@@ -289,8 +289,10 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DKDV_DROP_OCC : GATTN_DKDV_O
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
   // Key tiles near the start have the most query tiles below the diagonal.
-  const int kt = int(blockIdx.x) / BH;
-  const int bh = int(blockIdx.x) % BH;
+  const int BH8 = heads_padded(BH);
+  const int kt = int(blockIdx.x) / BH8;
+  const int bh = int(blockIdx.x) % BH8;
+  if (bh >= BH) return;  // grid padding (uniform in the workgroup, before any barrier)
   const int64_t base = slice_base<HS, STRIDED>(li, bh, H, T);
   const uint32_t slice_bytes = slice_bytes_of<HS, STRIDED>(li, T);
   const int rs = STRIDED ? int(li.st) : HS, rso = STRIDED ? int(lo.st) : HS;
@@ -557,8 +559,10 @@ __global__ __launch_bounds__(kThreads, DROP ? GATTN_DQ_DROP_OCC : GATTN_DQ_OCC) 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int nqt = (T + C::BM - 1) / C::BM;
-  const int qt = nqt - 1 - int(blockIdx.x) / BH;  // heaviest query tiles first
-  const int bh = int(blockIdx.x) % BH;
+  const int BH8 = heads_padded(BH);
+  const int qt = nqt - 1 - int(blockIdx.x) / BH8;  // heaviest query tiles first
+  const int bh = int(blockIdx.x) % BH8;
+  if (bh >= BH) return;  // grid padding (uniform in the workgroup, before any barrier)
   const int64_t base = slice_base<HS, STRIDED>(li, bh, H, T);
   const uint32_t slice_bytes = slice_bytes_of<HS, STRIDED>(li, T);
   const int rs = STRIDED ? int(li.st) : HS, rso = STRIDED ? int(lo.st) : HS;
@@ -724,7 +728,7 @@ hipError_t dkdv16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          int hs, float scale, Layout li, Layout lo, Layout lg, const Dropout& dr,
                          hipStream_t s) {
   const int bn = DkdvCfg<64>::BN;
-  const dim3 grid(unsigned(((T + bn - 1) / bn) * BH));
+  const dim3 grid(unsigned(((T + bn - 1) / bn) * heads_padded(BH)));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
   auto pick = [&](auto dropc) {
     constexpr bool D = decltype(dropc)::value;
@@ -743,7 +747,7 @@ hipError_t dq16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                        int T, int hs, float scale, Layout li, Layout lo, Layout lg,
                        const Dropout& dr, hipStream_t s) {
   const int bm = DqCfg<64>::BM;
-  const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
+  const dim3 grid(unsigned(((T + bm - 1) / bm) * heads_padded(BH)));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lg);
   auto pick = [&](auto dropc) {
     constexpr int D = decltype(dropc)::value;

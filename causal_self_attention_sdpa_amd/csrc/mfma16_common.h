@@ -287,6 +287,13 @@ __device__ inline void ring_loop(int n, F& step) {
   for (int t0 = 0; t0 < n; t0 += NS) ring_block<0, NS>(t0, n, step);
 }
 
+// Grid order of the training kernels: tile rank r (heaviest tiles first)
+// times the head count padded to a multiple of 8, plus the head.  The
+// dispatcher deals workgroups to the 8 XCDs in turn, so with the padded count
+// every tile of head bh runs on XCD bh % 8 and reads that head's rows through
+// one L2, for any B*H; a padding workgroup (head >= B*H) exits at once.
+__host__ __device__ inline int heads_padded(int BH) { return (BH + 7) & ~7; }
+
 // Element offset and byte span of slice bh of a tensor: through its Layout,
 // or, when STRIDED is false (contiguous (B, H, T, HS)), as bh*T*HS and T*HS*2
 // without the layout's division by H.

@@ -212,8 +212,10 @@ __global__ __launch_bounds__(kThreads) void fwd16_kernel(const uint16_t* __restr
   const int n = lane & 31, h = lane >> 5;
   const int nqt = (T + C::BM - 1) / C::BM;
   // Heaviest query tiles (most key tiles under the diagonal) first.
-  const int qt = nqt - 1 - int(blockIdx.x) / BH;
-  const int bh = int(blockIdx.x) % BH;
+  const int BH8 = heads_padded(BH);
+  const int qt = nqt - 1 - int(blockIdx.x) / BH8;
+  const int bh = int(blockIdx.x) % BH8;
+  if (bh >= BH) return;  // grid padding (uniform in the workgroup, before any barrier)
   const int64_t base = slice_base<HS, STRIDED>(li, bh, H, T);
   const uint32_t slice_bytes = slice_bytes_of<HS, STRIDED>(li, T);
   const int rs = STRIDED ? int(li.st) : HS;
@@ -306,7 +308,7 @@ hipError_t fwd16_launch(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         float* lse, uint64_t* keep, int BH, int H, int T, int hs, float scale,
                         Layout li, Layout lo, const Dropout& dr, hipStream_t s) {
   const int bm = FwdCfg<64>::BM;
-  const dim3 grid(unsigned(((T + bm - 1) / bm) * BH));
+  const dim3 grid(unsigned(((T + bm - 1) / bm) * heads_padded(BH)));
   const bool strided = !all_contiguous(H, T, hs, li, lo, lo);
   auto pick = [&](auto dropc) {
     constexpr bool D = decltype(dropc)::value;
