@@ -288,11 +288,18 @@ __device__ inline void ring_loop(int n, F& step) {
 }
 
 // Grid order of the training kernels: tile rank r (heaviest tiles first)
-// times the head count padded to a multiple of 8, plus the head.  The
-// dispatcher deals workgroups to the 8 XCDs in turn, so with the padded count
-// every tile of head bh runs on XCD bh % 8 and reads that head's rows through
-// one L2, for any B*H; a padding workgroup (head >= B*H) exits at once.
-__host__ __device__ inline int heads_padded(int BH) { return (BH + 7) & ~7; }
+// times the row length returned here, plus the head.  The dispatcher deals
+// workgroups to the 8 XCDs in turn, so with a multiple of 8 every tile of head
+// bh runs on XCD bh % 8 and reads that head's rows through one L2.  Whole
+// heads per XCD are then ceil(BH/8) on some XCDs and floor(BH/8) on others, so
+// the count is padded (padding workgroups, head >= BH, exit at once) only when
+// that costs at most 8/BH <= 1/32 of balance; a smaller count that is not a
+// multiple of 8 keeps the plain order, which spreads every head's tiles over
+// the XCDs but balances them exactly (12 heads padded to 16: XCDs 0-3 would
+// hold two heads, XCDs 4-7 one).
+__host__ __device__ inline int heads_padded(int BH) {
+  return BH % 8 == 0 || BH < 256 ? BH : (BH + 7) & ~7;
+}
 
 // Element offset and byte span of slice bh of a tensor: through its Layout,
 // or, when STRIDED is false (contiguous (B, H, T, HS)), as bh*T*HS and T*HS*2
