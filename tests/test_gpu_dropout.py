@@ -156,6 +156,11 @@ def test_dropout_gpt2_small_whole_layer(qkv_scale, p):
     assert not any(bad.values()), (where, "elements not within the bar", bad)
 
 
+def test_dropout_padded_head_grid():
+    """261 heads (the training kernels' grids pad them to 264): every slice."""
+    _check("bf16", 3, 87, 70, 64, 0.1)
+
+
 def test_dropout_robgpt_shape():
     """The RobGPT model's attention (12 heads of 32, 256 tokens, dropout 0.1),
     batch 8, every slice."""

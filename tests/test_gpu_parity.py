@@ -182,6 +182,20 @@ def test_bf16_gpt2_xl_heads():
     _sampled(12, 25, 1024, 64, 1.0, [(0, 0), (3, 24), (11, 12)], 3)
 
 
+def test_bf16_padded_head_grid_every_slice():
+    """B=3, H=87: 261 heads, at least 256 and not a multiple of 8, so the
+    training kernels' grids pad the head count to 264 (the padding workgroups
+    exit at once); every slice, the last head included, against the oracle."""
+    import oracle
+    B, H, T, hs = 3, 87, 70, 64
+    x = inputs(B, H, T, hs, "bf16", seed=12, workload="padded-heads")
+    s = default_scale(hs)
+    print(f"case bf16 padded head grid B={B} H={H} T={T} hs={hs}", flush=True)
+    got = gpu_fwd_bwd(x, "bf16", s)
+    ref = oracle.attention_backward(x["q"], x["k"], x["v"], x["do"], s)
+    check_close(got, ref, BF16_TOL, BF16_REL, where=f"bf16 {(B, H, T, hs)} every slice")
+
+
 def test_bf16_unit_variance_within_rounding_bound():
     """The derived rounding bound also holds (and is tighter than 2e-2 for
     small values) on unit-variance inputs."""

@@ -55,6 +55,7 @@ def _split_bthc(a: np.ndarray, H: int, parts: int):
     ("bf16", 2, 12, 256, 64),
     ("bf16", 3, 4, 200, 32),
     ("bf16", 1, 3, 77, 64),
+    ("bf16", 3, 87, 70, 64),  # 261 heads: the grid pads them to 264
     ("f32", 2, 3, 40, 24),
 ])
 def test_fused_qkv_matches_contiguous_bitwise_and_oracle(dtype, B, H, T, hs):
