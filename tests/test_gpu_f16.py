@@ -51,6 +51,11 @@ def test_f16_gpt2_small_shape():
     _check(12, 12, 1024, 64, slices=[(0, 0), (5, 7), (11, 11)], qkv_scale=0.5)
 
 
+def test_f16_gpt2_small_whole_layer():
+    """B=12, H=12, T=1024, hs=64, q/k/v x0.5: every slice of the layer."""
+    _check(12, 12, 1024, 64, qkv_scale=0.5)
+
+
 def test_f16_softmax_range_stress():
     """q/k/v x2.0: scores up to ~±60, the weights span many orders of magnitude."""
     _check(12, 12, 1024, 64, slices=[(0, 0), (6, 4)], qkv_scale=2.0)
