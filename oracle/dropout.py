@@ -44,17 +44,24 @@ def keep_scale(p: float) -> float:
     return 65536.0 / (65536.0 - t)
 
 
-def uniform16(bh: int, Tq: int, Tk: int, seed: int, offset: int) -> np.ndarray:
-    """u(i, j) for one slice (index bh = b*H + h), i < Tq, j < Tk, as uint32."""
-    i = np.arange(Tq, dtype=np.uint64)[:, None]
-    g = (np.arange(Tk, dtype=np.uint64) >> np.uint64(3))[None, :]
+def uniform16_window(bh: int, rows, key0: int, nkeys: int, seed: int, offset: int) -> np.ndarray:
+    """u(i, j) for one slice (index bh = b*H + h), i in `rows`, key0 <= j <
+    key0 + nkeys, as uint32 (len(rows), nkeys): the decisions of a window
+    without the whole T x T mask."""
+    i = np.asarray(rows, dtype=np.uint64)[:, None]
+    j = np.arange(key0, key0 + nkeys)
+    g = (j.astype(np.uint64) >> np.uint64(3))[None, :]
     words = philox4x32(i, g, np.uint64(bh), np.uint64(offset & 0xFFFFFFFF),
                        seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    j = np.arange(Tk)
-    w = np.stack(np.broadcast_arrays(*words), axis=0)  # (4, Tq, Tk)
-    sel = np.take_along_axis(w, np.broadcast_to(((j & 7) >> 1)[None, None, :], (1, Tq, Tk)),
-                             axis=0)[0]
+    w = np.stack(np.broadcast_arrays(*words), axis=0)  # (4, rows, nkeys)
+    sel = np.take_along_axis(w, np.broadcast_to(((j & 7) >> 1)[None, None, :],
+                                                (1, w.shape[1], nkeys)), axis=0)[0]
     return (sel >> ((j & 1) * 16).astype(np.uint32)) & np.uint32(0xFFFF)
+
+
+def uniform16(bh: int, Tq: int, Tk: int, seed: int, offset: int) -> np.ndarray:
+    """u(i, j) for one slice (index bh = b*H + h), i < Tq, j < Tk, as uint32."""
+    return uniform16_window(bh, np.arange(Tq), 0, Tk, seed, offset)
 
 
 def keep_mask(B: int, H: int, T: int, p: float, seed: int, offset: int, slices=None):
@@ -68,6 +75,12 @@ def keep_mask(B: int, H: int, T: int, p: float, seed: int, offset: int, slices=N
         for h in range(H):
             out[b, h] = uniform16(b * H + h, T, T, seed, offset) >= t
     return out
+
+
+def keep_window(bh: int, rows, key0: int, nkeys: int, p: float, seed: int,
+                offset: int) -> np.ndarray:
+    """keep(i, j) as bool for i in `rows`, key0 <= j < key0 + nkeys (slice bh)."""
+    return uniform16_window(bh, rows, key0, nkeys, seed, offset) >= threshold(p)
 
 
 def _slice_fwd(q, k, v, scale, z):

@@ -87,6 +87,28 @@ def test_mask_elements_are_halves_of_one_block():
             assert int(u[i, j]) == (x[(j & 7) >> 1] >> (16 * (j & 1))) & 0xFFFF
 
 
+def test_window_decisions_equal_the_mask_and_the_blocks():
+    """uniform16_window / keep_window (decisions of some rows against a key
+    window, for sequences too long for the whole mask) equal the slices of
+    the whole mask, and at the positions of the longest sequence the library
+    takes (rows up to 131063, keys from 131000) the halves of the single
+    blocks of their counters."""
+    seed, offset, bh, p = 0x0BAD_CAFE_1234_5678, 9, 3, 0.3
+    full = od.uniform16(bh, 60, 70, seed, offset)
+    rows = np.array([0, 5, 17, 59])
+    for key0, n in ((0, 70), (13, 40), (64, 6)):
+        win = od.uniform16_window(bh, rows, key0, n, seed, offset)
+        assert np.array_equal(win, full[rows][:, key0:key0 + n])
+        assert np.array_equal(od.keep_window(bh, rows, key0, n, p, seed, offset),
+                              win >= od.threshold(p))
+    big = np.array([131000, 131055, 131063])
+    win = od.uniform16_window(bh, big, 131000, 64, seed, offset)
+    for a, i in enumerate(big):
+        for b_, j in enumerate((131000, 131001, 131007, 131008, 131063)):
+            x = philox_block([int(i), j >> 3, bh, offset], [seed & 0xFFFFFFFF, seed >> 32], 32)
+            assert int(win[a, j - 131000]) == (x[(j & 7) >> 1] >> (16 * (j & 1))) & 0xFFFF
+
+
 def test_mask_rate_and_uniformity():
     """Over 4 slices of 512 x 512 values: the keep rate is within 5 standard
     deviations of 1 - t/65536, and the 16 leading-bit bins of the 16-bit values
