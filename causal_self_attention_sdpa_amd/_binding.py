@@ -244,9 +244,20 @@ def _view(t, name: str, shape, dtype):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if t.stride(3) != 1:
+    if t.shape[3] != 1 and t.stride(3) != 1:
         raise ValueError(f"{name}: the head dimension must be contiguous")
-    return ctypes.c_void_p(t.data_ptr()), tuple(int(x) for x in t.stride()[:3])
+    # The stride of a dimension of size 1 addresses nothing and torch leaves it
+    # arbitrary (0 for a view built from a broadcast array); pass canonical
+    # values so that views of one layout compare equal: the contiguous strides
+    # for a contiguous tensor (the library's contiguous kernels then run),
+    # else 0 for a batch or head dimension of size 1 and hs for one row.
+    B, H, T, hs = (int(x) for x in t.shape)
+    if t.is_contiguous():
+        st = (H * T * hs, T * hs, hs)
+    else:
+        st = tuple(int(x) for x in t.stride()[:3])
+        st = (0 if B == 1 else st[0], 0 if H == 1 else st[1], hs if T == 1 else st[2])
+    return ctypes.c_void_p(t.data_ptr()), st
 
 
 def _strides_arg(views, group: str):

@@ -19,7 +19,10 @@ def torch_dtype(dtype: str):
 
 def to_dev(a: np.ndarray, dtype: str):
     import torch
-    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch_dtype(dtype))
+    a = np.ascontiguousarray(a)
+    if not a.flags.writeable:  # a broadcast view: torch wants a writable array
+        a = a.copy()
+    return torch.from_numpy(a).to("cuda").to(torch_dtype(dtype))
 
 
 def gpu_fwd_bwd(x: dict, dtype: str, scale: float, use_stages: bool = False,

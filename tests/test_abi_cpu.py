@@ -358,3 +358,36 @@ def test_binding_keeps_a_call_on_one_device():
     with pytest.raises(ValueError, match="stream is on"):
         b._on(s1, t0, None, t0)
     assert b._on(s1, t1, None).value == 1234
+
+
+def test_binding_canonical_strides_for_size_one_dimensions():
+    """Strides of size-1 dimensions are arbitrary in torch (0 for a view of a
+    broadcast array): the binding passes canonical ones, so views of one
+    layout compare equal (stand-ins carrying shape and strides only)."""
+    import torch
+    from causal_self_attention_sdpa_amd import _binding as b
+
+    class View:
+        def __init__(self, shape, stride, contiguous):
+            self.shape, self._st, self._c = shape, stride, contiguous
+            self.is_cuda, self.dtype = True, torch.bfloat16
+
+        def stride(self, i=None):
+            return self._st if i is None else self._st[i]
+
+        def is_contiguous(self):
+            return self._c
+
+        def data_ptr(self):
+            return 4096
+
+    shape = (1, 1, 300, 64)
+    a = b._view(View(shape, (0, 0, 64, 1), True), "a", shape, torch.bfloat16)[1]
+    c = b._view(View(shape, (19200, 19200, 64, 1), True), "c", shape, torch.bfloat16)[1]
+    assert a == c == (19200, 19200, 64)
+    # a strided view (rows 3*C apart) with one batch and one head
+    d = b._view(View(shape, (7, 0, 192, 1), False), "d", shape, torch.bfloat16)[1]
+    assert d == (0, 0, 192)
+    one = (2, 3, 1, 64)
+    e = b._view(View(one, (64 * 5, 64, 0, 1), False), "e", one, torch.bfloat16)[1]
+    assert e == (320, 64, 64)

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from gpu_util import (check_close, default_scale, gpu_fwd_bwd, inputs, oracle_slices, pick,
-                      torch_dtype)
+                      to_dev, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 
@@ -169,3 +169,33 @@ def test_binding_rejects_mismatched_views():
         bad = torch.zeros(B * H * T * 32 + 64, dtype=torch.bfloat16, device="cuda")
         ov = bad.as_strided((B, H, T, hs), (H * T * 32, T * 32, 32, 1))
         ga.gattn_fwd_strided(q, q, q, ov, None, 0.125)
+
+
+def test_size_one_dimensions_with_any_stride():
+    """B = H = 1 tensors whose batch and head strides are 0 (as torch leaves a
+    view of a broadcast array) give the same bits through the strided and
+    dropout entry points as the canonical tensors."""
+    import torch
+    import causal_self_attention_sdpa_amd as ga
+    B, H, T, hs = 1, 1, 77, 64
+    x = inputs(B, H, T, hs, "bf16", seed=74, workload="size-one")
+    s = default_scale(hs)
+    print(f"case size-one strides B={B} H={H} T={T} hs={hs}", flush=True)
+    t = {n: to_dev(a, "bf16") for n, a in x.items()}
+    z = {n: a.as_strided(a.shape, (0, 0, hs, 1)) for n, a in t.items()}
+
+    def run(d):
+        o = torch.empty_like(t["q"])
+        lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+        ga.gattn_fwd_strided(d["q"], d["k"], d["v"], o, lse, s)
+        n = ga.gattn_bwd_workspace_bytes(B, H, T, hs, ga.BF16)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dq, dk, dv = (torch.empty_like(t["q"]) for _ in range(3))
+        ga.gattn_bwd_strided(d["q"], d["k"], d["v"], o, d["do"], lse, dq, dk, dv, s, ws)
+        od, ld = ga.attention_forward_dropout(d["q"], d["k"], d["v"], 0.2, 3, 1, s)
+        gd = ga.attention_backward_dropout(d["q"], d["k"], d["v"], od, d["do"], ld, 0.2, 3, 1, s)
+        torch.cuda.synchronize()
+        return (o, lse, dq, dk, dv, od, ld, *gd)
+
+    for i, (a, b) in enumerate(zip(run(z), run(t))):
+        assert torch.equal(a, b), i
