@@ -287,6 +287,68 @@ def test_backward_keep_decisions_exact(which, T, win, stored):
     assert np.all(val[..., ~vis] == 0)
 
 
+# The longest sequence the 16-bit dropout path takes: ceil(T/8) <= 16383 key
+# groups, so a keep buffer's byte offsets (block (I, G) at (I*ng + G)*8) reach
+# just below 2^31 on its last rows.
+LONG_T = 8 * 16383
+
+
+def test_forward_keep_decisions_and_keep_bytes_at_the_longest_sequence():
+    """T = 131064, one head: the forward's decisions against the last 64 keys,
+    read out of o through a one-hot v on every row, and the keep buffer's bits
+    for those keys on every row, equal the oracle's (keep_window); causal pairs
+    only (the buffer's bits above the diagonal are never written)."""
+    import torch
+    import causal_self_attention_sdpa_amd as ga
+    from oracle import dropout as od
+    T, hs, p, seed, off = LONG_T, 64, 0.3, 1357, 2
+    win = T - hs
+    print(f"case dropout forward keep read-out T={T} keys {win}..{T - 1}", flush=True)
+    q = torch.zeros((1, 1, T, hs), dtype=torch.bfloat16, device="cuda")
+    k = to_dev(inputs(1, 1, T, hs, "bf16", seed=105, workload="dropout-long")["k"], "bf16")
+    v = to_dev(_onehot_window(T, hs, win)[None, None], "bf16")
+    o, _, keep = ga.attention_forward_dropout(q, k, v, p, seed, off, need_lse=False,
+                                              return_keep=True)
+    torch.cuda.synchronize()
+    rows = np.arange(T)
+    kept = od.keep_window(0, rows, win, hs, p, seed, off)          # (T, 64)
+    vis = (win + np.arange(hs))[None, :] <= rows[:, None]
+    assert np.array_equal(o[0, 0].float().cpu().numpy() != 0, kept & vis)
+    ng = (T + 7) // 8
+    groups = win // 8 + np.arange(hs // 8)
+    byte = ((rows >> 3)[:, None] * ng + groups[None, :]) * 8 + (rows & 7)[:, None]
+    assert int(byte.max()) < 2 ** 31
+    by = keep.view(-1)[torch.from_numpy(byte.ravel()).to("cuda")].cpu().numpy().reshape(T, -1)
+    bits = ((by[:, :, None] >> np.arange(8)[None, None, :]) & 1).astype(bool).reshape(T, hs)
+    assert np.array_equal(bits & vis, kept & vis)
+
+
+@pytest.mark.parametrize("stored", [False, True], ids=["drawn", "stored"])
+@pytest.mark.parametrize("which", ["dk", "dv"])
+def test_backward_keep_decisions_at_the_longest_sequence(which, stored):
+    """T = 131064, one head: the decisions of the last 64 queries against every
+    key, read out of dk or dv as in test_backward_keep_decisions_exact, drawn by
+    the backward or read from the forward's keep buffer."""
+    from oracle import dropout as od
+    T, hs, p, seed, off, s = LONG_T, 64, 0.3, 91, 5, 0.125
+    win = T - hs
+    x = _grad_setup(1, 1, T, hs, which, win)
+    print(f"case dropout backward keep read-out {which} T={T} stored={stored}", flush=True)
+    dq, dk, dv, o, lse = _gpu_run(x, "bf16", s, p, seed, off, stored=stored)
+    rows = win + np.arange(hs)
+    kept = od.keep_window(0, rows, 0, T, p, seed, off)              # (64, T): keep[win+d][j]
+    vis = np.arange(T)[None, :] <= rows[:, None]
+    if which == "dv":
+        assert np.array_equal(dv[0, 0].T != 0, kept & vis)           # dv[j][d] = (P Z)[win+d][j]
+        return
+    zs = od.keep_scale(p)
+    D = 2 * zs * np.sum(kept & vis, axis=1) / (rows + 1)           # row term of each query
+    val = dk[0, 0].T / s                                           # dS[win+d][j]
+    mid = (zs - D[:, None]) / (rows[:, None] + 1)
+    assert np.array_equal((val > mid) & vis, kept & vis)
+    assert np.all(val[~vis] == 0)
+
+
 # ---------------------------------------------------------------- properties
 
 def test_p0_is_the_plain_path_bitwise():
