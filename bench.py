@@ -127,8 +127,44 @@ def measured_peaks(torch, dev):
         lib.gattn_probe_mfma_bf16(sink.data_ptr(), blocks, iters, sp)
     torch.cuda.synchronize()
     mfma = blocks * 4 * iters * 8 * 32768 * 5 / (time.perf_counter() - t0) / 1e12
+    # the vector ALU beside the matrix core (the library's issue probe): cost of
+    # a wave64 vector instruction in MFMA cycles (a saturated 32x32x16 bf16 MFMA,
+    # two wavefronts per SIMD, taken as 32), with two or one issuing wavefronts
+    # per SIMD, and MFMAs of one wavefront beside v_fma_f32 of another
+    pb, mi, vi = 256, 4000, 4000
+    sink8 = torch.empty(8 * pb, dtype=torch.float32, device=dev)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def t_issue(m_it, v_it, kind, roles, reps=5):
+        # best of `reps` launches, each bracketed by events on the launch stream
+        best = float("inf")
+        for rep in range(reps + 1):
+            ev0.record()
+            assert lib.gattn_probe_issue(sink8.data_ptr(), pb, m_it, v_it, kind, roles, sp) == 0
+            ev1.record()
+            ev1.synchronize()
+            if rep:
+                best = min(best, ev0.elapsed_time(ev1) * 1e-3)
+        return best
+
+    per_mfma = t_issue(mi, 0, 0, 1 | 4) / (2 * mi * 4)
+    valu = {}
+    for kind, name in ((0, "v_fma_f32"), (1, "v_mul_f32"), (2, "v_exp_f32")):
+        two = t_issue(0, vi, kind, 2 | 8) / (2 * vi * 16)
+        one = t_issue(0, vi, kind, 2) / (vi * 16)
+        valu[name] = {"two_wavefronts": round(32 * two / per_mfma, 2),
+                      "one_wavefront": round(32 * one / per_mfma, 2)}
+    coexec = {"mfma_alone_ms": round(1e3 * t_issue(mi, 0, 0, 1), 4),
+              "fma_alone_ms": round(1e3 * t_issue(0, vi, 0, 8), 4),
+              "both_ms": round(1e3 * t_issue(mi, vi, 0, 1 | 8), 4)}
     return {"bf16_gemm_tflops": round(gemm, 1), "copy_gbs": round(copy, 1),
             "mfma_loop_bf16_tflops": round(mfma, 1),
+            "valu_cycles_per_instruction": valu, "mfma_beside_valu": coexec,
+            "issue_probe": ("gattn_probe_issue: 256 x 8 wavefronts; 4000 x 4 MFMA 32x32x16 or "
+                            "4000 x 16 vector instructions per wavefront; cycles in MFMA units "
+                            "(32 per MFMA); mfma_beside_valu: MFMAs on wavefronts 0-3, v_fma_f32 "
+                            "on 4-7, alone and together"),
             "gemm": "torch.matmul bf16 8192x8192x8192", "copy": "1 GiB device-to-device",
             "mfma_loop": "gattn_probe_mfma_bf16: 2048 x 4 wavefronts x 128 x 8 MFMA 32x32x16"}
 

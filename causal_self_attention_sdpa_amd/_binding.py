@@ -84,6 +84,8 @@ def load_library():
     lib.gattn_dropout_mask.restype = i
     lib.gattn_probe_mfma_bf16.argtypes = [vp, i, i, vp]
     lib.gattn_probe_mfma_bf16.restype = i
+    lib.gattn_probe_issue.argtypes = [vp, i, i, i, i, i, vp]
+    lib.gattn_probe_issue.restype = i
     lib.gattn_status_string.argtypes = [i]
     lib.gattn_status_string.restype = ctypes.c_char_p
     _lib = lib

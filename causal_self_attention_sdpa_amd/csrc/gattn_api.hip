@@ -300,6 +300,14 @@ int gattn_probe_mfma_bf16(float* sink, int blocks, int iters, hipStream_t stream
   return status_of(gattn::mfma_loop(sink, blocks, iters, stream));
 }
 
+int gattn_probe_issue(float* sink, int blocks, int mfma_iters, int valu_iters, int kind,
+                      int roles, hipStream_t stream) {
+  if (sink == nullptr || blocks < 1 || mfma_iters < 0 || valu_iters < 0 || kind < 0 || kind > 2 ||
+      roles < 1 || roles > 15)
+    return GATTN_ERR_INVALID_ARG;
+  return status_of(gattn::issue_probe(sink, blocks, mfma_iters, valu_iters, kind, roles, stream));
+}
+
 int gattn_dropout_mask(uint8_t* keep, int B, int H, int T, float p, uint64_t seed,
                        uint32_t offset, hipStream_t stream) {
   if (keep == nullptr || B < 1 || H < 1 || T < 1) return GATTN_ERR_INVALID_ARG;

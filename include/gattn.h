@@ -345,6 +345,24 @@ int gattn_dropout_mask(uint8_t* keep, int B, int H, int T, float p, uint64_t see
  */
 int gattn_probe_mfma_bf16(float* sink, int blocks, int iters, hipStream_t stream);
 
+/*
+ * Diagnostic, not part of attention: what vector-ALU work costs beside the
+ * matrix core.  `blocks` workgroups of 8 wavefronts, one per CU (96 KB of LDS
+ * each keeps a second one off; two wavefronts per SIMD: wavefronts 0-3 and
+ * 4-7 each span the CU's four SIMDs) run register-only loops chosen by
+ * `roles`: bit 0, wavefronts 0-3 run mfma_iters rounds of 4 independent bf16
+ * MFMAs (32x32x16); bit 1, wavefronts 0-3 run valu_iters rounds of 16
+ * independent wave64 instructions of `kind` (0 v_fma_f32, 1 v_mul_f32,
+ * 2 v_exp_f32); bits 2 and 3, the same for wavefronts 4-7.  Each wavefront
+ * writes one float to sink (device buffer of 8*blocks floats).  Timing
+ * launches of different roles gives the cost of a vector instruction in MFMA
+ * cycles, with one or two issuing wavefronts per SIMD, and how much of it
+ * runs beside another wavefront's MFMAs.  INVALID_ARG for sink NULL,
+ * blocks < 1, a negative count, kind outside 0..2 or roles outside 1..15.
+ */
+int gattn_probe_issue(float* sink, int blocks, int mfma_iters, int valu_iters, int kind,
+                      int roles, hipStream_t stream);
+
 /* Static, human-readable name of a gattn_status value. */
 const char* gattn_status_string(int status);
 

@@ -296,6 +296,14 @@ def test_probe_validation(lib):
     assert lib.gattn_probe_mfma_bf16(None, 4, 4, None) == INVALID
     assert lib.gattn_probe_mfma_bf16(P, 0, 4, None) == INVALID
     assert lib.gattn_probe_mfma_bf16(P, 4, 0, None) == INVALID
+    assert lib.gattn_probe_issue(None, 4, 4, 4, 0, 1, None) == INVALID
+    assert lib.gattn_probe_issue(P, 0, 4, 4, 0, 1, None) == INVALID
+    assert lib.gattn_probe_issue(P, 4, -1, 4, 0, 1, None) == INVALID
+    assert lib.gattn_probe_issue(P, 4, 4, -1, 0, 1, None) == INVALID
+    for kind in (-1, 3):
+        assert lib.gattn_probe_issue(P, 4, 4, 4, kind, 1, None) == INVALID
+    for roles in (0, 16):
+        assert lib.gattn_probe_issue(P, 4, 4, 4, 0, roles, None) == INVALID
 
 
 def test_header_is_plain_c_and_the_c_caller_links(tmp_path):
