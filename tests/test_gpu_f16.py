@@ -61,6 +61,11 @@ def test_f16_softmax_range_stress():
     _check(12, 12, 1024, 64, slices=[(0, 0), (6, 4)], qkv_scale=2.0)
 
 
+def test_f16_softmax_range_stress_whole_layer():
+    """q/k/v x2.0 at B=12, H=12, T=1024, hs=64: every slice of the layer."""
+    _check(12, 12, 1024, 64, qkv_scale=2.0, seed=84)
+
+
 def test_f16_char_level_shape():
     _check(64, 6, 256, 64, slices=[(0, 0), (17, 3), (63, 5)])
 
