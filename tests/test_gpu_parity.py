@@ -162,6 +162,12 @@ def test_bf16_gpt2_small_whole_layer(qkv_scale):
     _whole_layer(12, 12, 1024, 64, qkv_scale, 2)
 
 
+def test_bf16_gpt2_xl_whole_layer():
+    """B=12, H=25, T=1024, hs=64 (300 heads: the grid pads to 304): all 300
+    slices of layer 0."""
+    _whole_layer(12, 25, 1024, 64, 1.0, 3)
+
+
 def test_bf16_char_level_full_size():
     """B=64, H=6, T=256, hs=64: full launch, sampled slices."""
     _sampled(64, 6, 256, 64, 1.0, [(0, 0), (17, 3), (63, 5)], 1)
